@@ -1,0 +1,37 @@
+"""The seeded input generator: deterministic, shaped and scaled as stated."""
+import numpy as np
+
+import synth
+
+
+def test_deterministic_and_distinct_seeds():
+    a = synth.normal_bf16((4, 300), 1.0, 5)
+    b = synth.normal_bf16((4, 300), 1.0, 5)
+    c = synth.normal_bf16((4, 300), 1.0, 6)
+    assert a.dtype == np.uint16 and a.shape == (4, 300)
+    assert np.array_equal(a, b) and not np.array_equal(a, c)
+
+
+def test_chunked_draw_equals_single_draw():
+    n = (1 << 20) + 12345
+    got = synth.normal_bf16((n,), 0.5, 77)
+    rng = np.random.Generator(np.random.PCG64(77))
+    x = rng.standard_normal(size=n, dtype=np.float32) * np.float32(0.5)
+    assert np.array_equal(got, synth.f32_to_bf16_bits(x))
+
+
+def test_workload_scales():
+    X, W, b = synth.make_inputs(16, 512, 4096, True, 1)
+    f = lambda u: (u.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert abs(f(X).std() - 1.0) < 0.02
+    assert abs(f(W).std() * np.sqrt(4096) - 1.0) < 0.02
+    assert abs(f(b).std() - np.sqrt(0.02)) < 0.02
+    assert [w.M for w in synth.WORKLOADS] == [16, 16, 64, 8192, 4096]
+    assert synth.WORKLOADS[0].alg_bytes() == 17104896
+    assert synth.WORKLOADS[4].alg_flops() == 549755813888
+
+
+def test_bf16_rounding_of_inputs():
+    # halfway cases go to the even neighbour
+    v = np.array([1.00390625, 1.01171875, -1.00390625], dtype=np.float32)
+    assert synth.f32_to_bf16_bits(v).tolist() == [0x3F80, 0x3F82, 0xBF80]
