@@ -1,0 +1,229 @@
+"""Benchmark the dense projection hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload IDX]
+
+A step is one projection Y = epi(X . W^T + bias) over one batch of synthetic
+input (one proj_run: plan lookup, kernel, fused epilogue), replayed from a
+HIP graph captured through the library (proj_graph_capture).  Steps cycle
+over P rotating buffer sets (distinct allocations of X, W, bias, Y) whose
+total size exceeds the 256 MiB last-level cache, so W streams from HBM as it
+would in a model.  Inputs are resident in HBM before the timed region.
+
+Timing: HIP events recorded on the stream the graph is launched on, around
+exactly K steps, with device synchronisation on both sides.  The dominant
+(only) kernel of a step is the projection kernel; its average duration is
+taken as the timed region divided by K (this includes the small gaps between
+graph nodes, so it is an upper bound on the kernel's own duration).
+
+Prints ONE JSON line.  Default workload: M=16 K=8192 N=8192, bias, bf16 out.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "TFLOP/s + achieved HBM GB/s (% roofline) for bf16 Y=X·Wᵀ, M=16 K=8192"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+LLC_BYTES = 256 << 20          # last-level (Infinity) cache
+
+
+def kernel_sources_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "dense_linear_projection_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload_name: str, launches_per_step: int):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "counters_%s.json" % workload_name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        c = json.load(f)
+    if c.get("src_hash") != kernel_sources_hash():
+        return None
+    kib = (c["fetch_kib_per_dispatch"] + c["write_kib_per_dispatch"]) * c["copy_scale"]
+    return kib * 1024.0 * launches_per_step / launches_per_step
+
+
+def cpu_baseline(w, X, W, b, min_seconds: float):
+    """The oracle as it stands, on the host cores: repeat the whole workload
+    (or a fixed slice of its rows for big ones) until min_seconds pass."""
+    import numpy as np
+    import oracle
+    cores = oracle.default_threads()
+    # rows of Y in the sample: all rows when the workload is small enough
+    macs_per_row = w.N * w.K
+    rows = w.M if w.M * macs_per_row <= 4e9 else max(1, int(2e9 // macs_per_row))
+    Xs = np.ascontiguousarray(X[:rows])
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.proj_f64(Xs, W, b, w.epi, nthreads=cores)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    frac = rows / w.M
+    bytes_done = w.alg_bytes() * frac * reps
+    return {
+        "value": round(bytes_done / el / 1e9, 3),
+        "unit": "GB/s",
+        "tflops": round(w.alg_flops() * frac * reps / el / 1e12, 6),
+        "cores": cores,
+        "kind": "oracle",
+        "sample": "%d of %d rows of Y (all N columns, full K), %d repetition(s), %.1f s, fp64 C oracle"
+                  % (rows, w.M, reps, el),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", type=int, default=1, help="index into synth.WORKLOADS (0..4)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--graph-calls", type=int, default=0, help="calls per captured graph (0: auto)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the projection path is single-GPU in this build "
+              "(sharding across GPUs is designed, not built). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import dense_linear_projection_amd as dlp
+    import synth
+
+    if not os.path.exists(dlp.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+
+    w = synth.WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    ctx = dlp.proj_create(0)
+
+    X, W, b = synth.workload_inputs(w)
+    set_bytes = w.alg_bytes()
+    P = max(1, -(-(2 * LLC_BYTES) // set_bytes))      # working set > 2x the LLC
+    P = min(P, 16)
+    to_dev = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    W0 = to_dev(W)
+    b0 = to_dev(b) if b is not None else None
+    Xs, Ws, bs, Ys = [], [], [], []
+    out_t = torch.float32 if w.out_dtype == synth.OUT_F32 else torch.bfloat16
+    for p in range(P):
+        Xs.append(to_dev(synth.normal_bf16((w.M, w.K), 1.0, 1000 + w.index + 100 * p)))
+        Ws.append(W0 if p == 0 else W0.clone())
+        bs.append(None if b0 is None else (b0 if p == 0 else b0.clone()))
+        Ys.append(torch.empty((w.M, w.N), dtype=out_t, device=dev))
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for p in range(P):                       # plan tuning happens on the first call
+            dlp.proj_run(ctx, Xs[p], Ws[p], bs[p], w.epi, Ys[p], stream=stream)
+    stream.synchronize()
+    plan = dlp.proj_get_plan(ctx, w.M, w.N, w.K, w.epi, w.out_dtype)
+
+    # one graph holds R calls cycling over the P buffer sets
+    R = args.graph_calls or max(P, min(args.steps, 200) // P * P)
+    idx = [i % P for i in range(R)]
+    g = dlp.proj_graph_capture(ctx, [Xs[i] for i in idx], [Ws[i] for i in idx],
+                               [bs[i] for i in idx] if b0 is not None else None,
+                               [Ys[i] for i in idx], w.epi, stream=stream)
+    tail = args.steps % R
+    g_tail = None
+    if tail:
+        g_tail = dlp.proj_graph_capture(ctx, [Xs[i % P] for i in range(tail)], [Ws[i % P] for i in range(tail)],
+                                        [bs[i % P] for i in range(tail)] if b0 is not None else None,
+                                        [Ys[i % P] for i in range(tail)], w.epi, stream=stream)
+
+    # warmup (untimed)
+    for _ in range(max(1, args.warmup // R)):
+        dlp.proj_graph_launch(g, stream=stream)
+    stream.synchronize()
+    torch.cuda.synchronize()
+
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps // R):
+        dlp.proj_graph_launch(g, stream=stream)
+    if g_tail is not None:
+        dlp.proj_graph_launch(g_tail, stream=stream)
+    e1.record(stream)
+    e1.synchronize()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    ms_per_step = ms / args.steps
+    sec = ms_per_step / 1e3
+
+    gbs = w.alg_bytes() / sec / 1e9
+    tflops = w.alg_flops() / sec / 1e12
+    hbm_bound = w.M <= 64
+    traffic = load_traffic(w.name, 1)
+    if hbm_bound:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": traffic}
+    roof["kernel"] = plan.split(" ")[0]
+    roof["avg_kernel_us"] = round(ms_per_step * 1e3, 3)
+    roof["alg_bytes_per_launch"] = w.alg_bytes()
+    roof["alg_flops_per_launch"] = w.alg_flops()
+
+    dlp.proj_graph_destroy(g)
+    if g_tail is not None:
+        dlp.proj_graph_destroy(g_tail)
+    dlp.proj_destroy(ctx)
+
+    line = {
+        "metric": METRIC,
+        "value": round(gbs, 1) if hbm_bound else round(tflops, 2),
+        "unit": "GB/s" if hbm_bound else "TFLOP/s",
+        "tflops": round(tflops, 2),
+        "gbs": round(gbs, 1),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "epilogue": w.epi,
+                   "out_dtype": "fp32" if w.out_dtype == synth.OUT_F32 else "bf16",
+                   "accumulate": "fp32", "rotating_sets": P, "graph_calls": R, "plan": plan},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, X, W, b, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,88 @@
+// common.hpp -- shared device types and the fused epilogue for libproj
+// kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace proj {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+
+enum Epi { EPI_NONE = 0, EPI_BIAS = 1, EPI_GELU = 2, EPI_BIAS_GELU = 3 };
+enum Out { OUT_F32 = 0, OUT_BF16 = 1 };
+
+// Everything a kernel needs to know about one call.
+struct Args {
+    const uint16_t *X;     // bf16 [M, K]
+    const uint16_t *W;     // bf16 [N, K]
+    const uint16_t *bias;  // bf16 [N] or nullptr
+    void *Y;               // fp32 / bf16 [M, N]
+    int64_t M, N, K;
+    int epi, out;
+    float *ws;             // split-K partials (library-owned)
+    unsigned *counters;    // split-K completion counters, zero between calls
+    const uint16_t *zeros; // >= 64 zero bytes in device memory, for masked loads
+};
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// GELU, tanh form: 0.5 v (1 + tanh(u)) with u = sqrt(2/pi) (v + 0.044715 v^3),
+// evaluated as v / (1 + exp(-2u)) -- the same function, one exponential.
+// The exponential overflows to +inf for very negative v, giving -0; it goes to
+// 0 for large v, giving v.  NaN propagates.
+__device__ __forceinline__ float gelu_tanh(float v) {
+    const float c2 = 2.0f * 0.7978845608028654f;  // 2 * sqrt(2/pi)
+    float u2 = c2 * (v + 0.044715f * v * v * v);
+    return v / (1.0f + __expf(-u2));
+}
+
+// bias (fp32-widened bf16) is added to the finished fp32 sum, then GELU.
+__device__ __forceinline__ float apply_epilogue(float acc, int epi, float bias) {
+    float v = acc;
+    if (epi & 1) v += bias;
+    if (epi & 2) v = gelu_tanh(v);
+    return v;
+}
+
+// fp32 -> bf16 bits, round to nearest even (hardware conversion on gfx950;
+// NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
+    __bf16 h = static_cast<__bf16>(v);
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ void store_out(void *Y, int out, int64_t idx, float v) {
+    if (out == OUT_F32)
+        static_cast<float *>(Y)[idx] = v;
+    else
+        static_cast<uint16_t *>(Y)[idx] = f32_to_bf16_bits(v);
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 load16(const uint16_t *p) {
+    return *reinterpret_cast<const bf16x8 *>(p);
+}
+
+// 16-byte global -> LDS copy without a register round trip
+// (global_load_lds_dwordx4): lane i of the wave writes lds_wave_base + 16*i.
+// lds_wave_base must be the same for the whole wave.
+__device__ __forceinline__ void dma16(const void *src, void *lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(src, lds_wave_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ bf16x8 load16_nt(const uint16_t *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(p));
+}
+
+}  // namespace proj

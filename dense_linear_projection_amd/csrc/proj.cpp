@@ -1,0 +1,581 @@
+// proj.cpp -- the C ABI of libproj (declared in include/proj.h): argument
+// checks, the per-context workspace, the measured plan cache and HIP-graph
+// capture of repeated calls.
+//
+// Plan choice follows the rule that a method wins only at a given size and
+// that the choice is made by measuring, not by thresholds fitted to one
+// machine (worklog "How I made Muse's GPU projections 1.32x faster in the
+// Open Kernel Challenge", section "I started picking a method based on the
+// job"; page "blackroom" on Devpost, sections "How we built it" and "What we
+// learned"): on the first uncaptured call for a shape, every compiled kernel
+// variant valid for the shape is timed on the caller's buffers and the
+// fastest is kept.  Under stream capture nothing may be timed or
+// synchronised, so an untimed default plan is used until a later uncaptured
+// tune.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "../../include/proj.h"
+#include "kernels.hpp"
+
+using namespace proj;
+
+namespace {
+
+constexpr uint32_t kMagic = 0x50524f4au;   // live context
+constexpr uint32_t kDead = 0xdeadbeefu;    // destroyed context
+constexpr size_t kWorkspaceBytes = 64ull << 20;
+constexpr size_t kCounters = 1u << 20;
+constexpr size_t kZeroBytes = 256;
+constexpr size_t kFlushBytes = 512ull << 20;  // larger than the last-level cache
+
+struct Key {
+    int64_t M, N, K;
+    int epi, out, aligned;
+    bool operator<(const Key &o) const {
+        return std::tie(M, N, K, epi, out, aligned) < std::tie(o.M, o.N, o.K, o.epi, o.out, o.aligned);
+    }
+};
+
+enum Kind { KIND_SKINNY = 0, KIND_GEMM = 1, KIND_GENERIC = 2 };
+
+struct Candidate {
+    Kind kind;
+    int variant;  // index into the kernel table
+    int splits;   // skinny only
+    std::string name;
+};
+
+struct Plan {
+    Candidate cand;
+    bool tuned;
+    float us;  // measured median (tuned plans)
+};
+
+}  // namespace
+
+struct proj_ctx {
+    uint32_t magic;
+    int device;
+    float *ws;
+    unsigned *counters;
+    uint16_t *zeros;
+    void *flush;
+    std::map<Key, Plan> plans;
+    std::mutex mu;
+    std::string err;
+};
+
+struct proj_graph {
+    uint32_t magic;
+    int device;
+    hipGraph_t graph;
+    hipGraphExec_t exec;
+};
+
+namespace {
+
+bool env_flag(const char *name, bool dflt) {
+    const char *v = std::getenv(name);
+    if (!v || !*v) return dflt;
+    return !(v[0] == '0' || v[0] == 'n' || v[0] == 'N' || v[0] == 'f' || v[0] == 'F');
+}
+
+void set_err(proj_ctx *c, const char *fmt, ...) {
+    if (!c) return;
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    c->err = buf;
+}
+
+proj_status hip_fail(proj_ctx *c, const char *what, hipError_t e) {
+    set_err(c, "%s: %s", what, hipGetErrorString(e));
+    return PROJ_ERR_HIP;
+}
+
+class DeviceGuard {
+   public:
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&prev_) != hipSuccess) prev_ = -1;
+        if (prev_ != dev) hipSetDevice(dev);
+    }
+    ~DeviceGuard() {
+        int cur = -1;
+        if (prev_ >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev_) hipSetDevice(prev_);
+    }
+
+   private:
+    int prev_ = -1;
+};
+
+int mt_for(int64_t M) {
+    const int64_t need = (M + 15) / 16;
+    return need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 0;
+}
+
+int64_t skinny_tiles(const SkinnyVariant &v, int64_t N) { return (N + 16 * v.nt - 1) / (16 * v.nt); }
+
+size_t skinny_ws_bytes(const SkinnyVariant &v, int64_t N, int S) {
+    if (S <= 1) return 0;
+    return static_cast<size_t>(skinny_tiles(v, N)) * S * v.mt * v.nt * 256 * sizeof(float);
+}
+
+std::string skinny_name(const SkinnyVariant &v, int S) {
+    char b[96];
+    snprintf(b, sizeof b, "skinny_mt%d_nt%d_w%d_u%d%s_s%d", v.mt, v.nt, v.waves, v.unroll,
+             v.nontemporal ? "_ntl" : "", S);
+    return b;
+}
+
+std::string gemm_name(const GemmVariant &v) {
+    char b[96];
+    snprintf(b, sizeof b, "gemm_%dx%dx%d_w%dx%d", v.bm, v.bn, v.bk, v.waves_m, v.waves_n);
+    return b;
+}
+
+// Every compiled variant that can run this shape correctly.  These are
+// validity rules (operand alignment, tile coverage of M, workspace size),
+// not performance guesses; the measurement picks among them.
+std::vector<Candidate> candidates(const Key &k) {
+    std::vector<Candidate> out;
+    if (k.aligned && k.K > 0) {
+        const int mt = mt_for(k.M);
+        if (mt > 0) {
+            const int64_t T = (k.K + 31) / 32;
+            for (int i = 0; i < kNumSkinnyVariants; ++i) {
+                const SkinnyVariant &v = kSkinnyVariants[i];
+                if (v.mt != mt) continue;
+                const int64_t tiles = skinny_tiles(v, k.N);
+                for (int S : {1, 2, 3, 4, 6, 8, 16}) {
+                    if (S > 1 && (S > T || static_cast<size_t>(tiles) > kCounters)) continue;
+                    if (skinny_ws_bytes(v, k.N, S) > kWorkspaceBytes) continue;
+                    if (tiles * S > 0x7fffffff) continue;
+                    out.push_back({KIND_SKINNY, i, S, skinny_name(v, S)});
+                }
+            }
+        }
+        for (int i = 0; i < kNumGemmVariants; ++i) {
+            const GemmVariant &v = kGemmVariants[i];
+            if (k.K % v.bk != 0) continue;
+            out.push_back({KIND_GEMM, i, 1, gemm_name(v)});
+        }
+    }
+    if (out.empty()) out.push_back({KIND_GENERIC, 0, 1, "generic"});
+    return out;
+}
+
+// The untimed plan used under stream capture or with PROJ_TUNE=0.
+Candidate default_candidate(const Key &k) {
+    std::vector<Candidate> c = candidates(k);
+    auto find = [&](const char *name) -> const Candidate * {
+        for (const Candidate &x : c)
+            if (x.name == name) return &x;
+        return nullptr;
+    };
+    if (mt_for(k.M) > 0) {
+        // smallest split count that gives at least one workgroup per CU
+        for (const Candidate &x : c) {
+            if (x.kind != KIND_SKINNY) continue;
+            const SkinnyVariant &v = kSkinnyVariants[x.variant];
+            if (v.nt != 1 || v.waves != 8 || v.unroll != 4 || v.nontemporal) continue;
+            if (skinny_tiles(v, k.N) * x.splits >= 256 || x.splits == 16) return x;
+        }
+    }
+    if (const Candidate *g = find("gemm_256x256x64_w2x2")) return *g;
+    for (const Candidate &x : c)
+        if (x.kind == KIND_GEMM) return x;
+    return c.front();
+}
+
+Args make_args(proj_ctx *c, const void *X, const void *W, const void *bias, int epi, int64_t M, int64_t N,
+               int64_t K, void *Y, int out) {
+    Args a;
+    a.X = static_cast<const uint16_t *>(X);
+    a.W = static_cast<const uint16_t *>(W);
+    a.bias = static_cast<const uint16_t *>(bias);
+    a.Y = Y;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.epi = epi;
+    a.out = out;
+    a.ws = c->ws;
+    a.counters = c->counters;
+    a.zeros = c->zeros;
+    return a;
+}
+
+hipError_t launch(const Candidate &cand, const Args &a, hipStream_t st) {
+    switch (cand.kind) {
+        case KIND_SKINNY: return kSkinnyVariants[cand.variant].launch(a, cand.splits, st);
+        case KIND_GEMM: return kGemmVariants[cand.variant].launch(a, st);
+        default: return launch_generic(a, st);
+    }
+}
+
+proj_status check_args(proj_ctx *c, const void *X, const void *W, const void *bias, int epi, int64_t M,
+                       int64_t N, int64_t K, void *Y, int out) {
+    if (!c) return PROJ_ERR_INVALID_ARG;
+    if (c->magic == kDead) return PROJ_ERR_DESTROYED;
+    if (c->magic != kMagic) return PROJ_ERR_INVALID_ARG;
+    if (M < 0 || N < 0 || K < 0) {
+        set_err(c, "negative size M=%lld N=%lld K=%lld", (long long)M, (long long)N, (long long)K);
+        return PROJ_ERR_INVALID_ARG;
+    }
+    if (epi < PROJ_EPI_NONE || epi > PROJ_EPI_BIAS_GELU_TANH) {
+        set_err(c, "unknown epilogue %d", epi);
+        return PROJ_ERR_INVALID_ARG;
+    }
+    if (out != PROJ_OUT_F32 && out != PROJ_OUT_BF16) {
+        set_err(c, "unknown output dtype %d", out);
+        return PROJ_ERR_INVALID_ARG;
+    }
+    if (M == 0 || N == 0) return PROJ_OK;
+    if (!Y) {
+        set_err(c, "Y is NULL");
+        return PROJ_ERR_INVALID_ARG;
+    }
+    if (K > 0 && (!X || !W)) {
+        set_err(c, "X or W is NULL");
+        return PROJ_ERR_INVALID_ARG;
+    }
+    if ((epi & 1) && !bias) {
+        set_err(c, "epilogue %d needs a bias, got NULL", epi);
+        return PROJ_ERR_INVALID_ARG;
+    }
+    const uintptr_t yal = out == PROJ_OUT_F32 ? 4 : 2;
+    if (reinterpret_cast<uintptr_t>(Y) % yal || reinterpret_cast<uintptr_t>(X) % 2 ||
+        reinterpret_cast<uintptr_t>(W) % 2 || reinterpret_cast<uintptr_t>(bias) % 2) {
+        set_err(c, "a pointer is not aligned to its element size");
+        return PROJ_ERR_INVALID_ARG;
+    }
+    if (M > (int64_t(1) << 40) / (N > 0 ? N : 1)) {
+        set_err(c, "M*N too large");
+        return PROJ_ERR_UNSUPPORTED;
+    }
+    return PROJ_OK;
+}
+
+Key make_key(const void *X, const void *W, int epi, int64_t M, int64_t N, int64_t K, int out) {
+    const bool al = (reinterpret_cast<uintptr_t>(X) % 16 == 0) && (reinterpret_cast<uintptr_t>(W) % 16 == 0) &&
+                    (K % 8 == 0);
+    return Key{M, N, K, epi, out, al ? 1 : 0};
+}
+
+bool capturing(hipStream_t st) {
+    hipStreamCaptureStatus s = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &s) != hipSuccess) return false;
+    return s != hipStreamCaptureStatusNone;
+}
+
+// Time every candidate on the caller's buffers; returns the winner.  The
+// last-level cache is flushed before each timed run when the operands could
+// fit in it, so small shapes are timed as they run from HBM.
+proj_status tune(proj_ctx *c, const Key &k, const Args &a, hipStream_t st, Plan &plan) {
+    std::vector<Candidate> cands = candidates(k);
+    const size_t bytes = static_cast<size_t>(2 * (k.M + k.N) * k.K);
+    const bool flush = bytes < kFlushBytes;
+    if (flush && !c->flush) {
+        if (hipMalloc(&c->flush, kFlushBytes) != hipSuccess) c->flush = nullptr;
+    }
+    hipEvent_t e0, e1;
+    if (hipEventCreate(&e0) != hipSuccess) return hip_fail(c, "hipEventCreate", hipGetLastError());
+    if (hipEventCreate(&e1) != hipSuccess) {
+        hipEventDestroy(e0);
+        return hip_fail(c, "hipEventCreate", hipGetLastError());
+    }
+    const int reps = 5;
+    float best = 1e30f;
+    int best_i = -1;
+    for (size_t i = 0; i < cands.size(); ++i) {
+        if (launch(cands[i], a, st) != hipSuccess) {  // warm-up; skip variants that cannot launch
+            (void)hipGetLastError();
+            continue;
+        }
+        std::vector<float> t;
+        bool ok = true;
+        for (int r = 0; r < reps && ok; ++r) {
+            if (flush && c->flush) hipMemsetAsync(c->flush, r & 0xff, kFlushBytes, st);
+            hipEventRecord(e0, st);
+            ok = launch(cands[i], a, st) == hipSuccess;
+            hipEventRecord(e1, st);
+            float ms = 0.f;
+            if (ok && hipEventSynchronize(e1) == hipSuccess && hipEventElapsedTime(&ms, e0, e1) == hipSuccess)
+                t.push_back(ms * 1000.f);
+            else
+                ok = false;
+        }
+        if (!ok || t.empty()) {
+            (void)hipGetLastError();
+            continue;
+        }
+        std::sort(t.begin(), t.end());
+        const float med = t[t.size() / 2];
+        if (med < best) {
+            best = med;
+            best_i = static_cast<int>(i);
+        }
+    }
+    hipEventDestroy(e0);
+    hipEventDestroy(e1);
+    if (best_i < 0) {
+        set_err(c, "no candidate could be launched");
+        return PROJ_ERR_HIP;
+    }
+    plan = Plan{cands[best_i], true, best};
+    // leave the winner's result in Y
+    hipError_t e = launch(plan.cand, a, st);
+    if (e != hipSuccess) return hip_fail(c, "launch", e);
+    return PROJ_OK;
+}
+
+proj_status run_impl(proj_ctx *c, const void *X, const void *W, const void *bias, int epi, int64_t M, int64_t N,
+                     int64_t K, void *Y, int out, void *stream, bool force_tune) {
+    proj_status s = check_args(c, X, W, bias, epi, M, N, K, Y, out);
+    if (s != PROJ_OK || M == 0 || N == 0) return s;
+    DeviceGuard g(c->device);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const Key k = make_key(X, W, epi, M, N, K, out);
+    const Args a = make_args(c, X, W, bias, epi, M, N, K, Y, out);
+    const bool cap = capturing(st);
+    if (force_tune && cap) {
+        set_err(c, "cannot tune while the stream is capturing");
+        return PROJ_ERR_NOT_TUNED;
+    }
+    std::lock_guard<std::mutex> lock(c->mu);
+    auto it = c->plans.find(k);
+    if (it == c->plans.end() || (force_tune && !it->second.tuned)) {
+        Plan p;
+        if (!cap && (force_tune || env_flag("PROJ_TUNE", true))) {
+            s = tune(c, k, a, st, p);
+            if (s != PROJ_OK) return s;
+            c->plans[k] = p;
+            return PROJ_OK;  // tune() already left the winner's result in Y
+        }
+        p = Plan{default_candidate(k), false, 0.f};
+        it = c->plans.insert_or_assign(k, p).first;
+    } else if (force_tune) {
+        // already tuned: just run it
+    }
+    hipError_t e = launch(it->second.cand, a, st);
+    if (e != hipSuccess) return hip_fail(c, "launch", e);
+    return PROJ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+proj_status proj_create(proj_ctx **out, int device) {
+    if (!out) return PROJ_ERR_INVALID_ARG;
+    *out = nullptr;
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) return PROJ_ERR_HIP;
+    if (device < 0 || device >= n) return PROJ_ERR_INVALID_ARG;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) != hipSuccess) return PROJ_ERR_HIP;
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return PROJ_ERR_UNSUPPORTED;
+    DeviceGuard g(device);
+    proj_ctx *c = new (std::nothrow) proj_ctx();
+    if (!c) return PROJ_ERR_NO_MEMORY;
+    c->magic = kMagic;
+    c->device = device;
+    c->ws = nullptr;
+    c->counters = nullptr;
+    c->zeros = nullptr;
+    c->flush = nullptr;
+    bool ok = hipMalloc(&c->ws, kWorkspaceBytes) == hipSuccess &&
+              hipMalloc(&c->counters, kCounters * sizeof(unsigned)) == hipSuccess &&
+              hipMalloc(&c->zeros, kZeroBytes) == hipSuccess &&
+              hipMemset(c->counters, 0, kCounters * sizeof(unsigned)) == hipSuccess &&
+              hipMemset(c->zeros, 0, kZeroBytes) == hipSuccess;
+    for (int i = 0; ok && i < kNumGemmVariants; ++i) ok = kGemmVariants[i].prepare() == hipSuccess;
+    ok = ok && hipDeviceSynchronize() == hipSuccess;
+    if (!ok) {
+        hipFree(c->ws);
+        hipFree(c->counters);
+        hipFree(c->zeros);
+        delete c;
+        return PROJ_ERR_HIP;
+    }
+    *out = c;
+    return PROJ_OK;
+}
+
+proj_status proj_run(proj_ctx *ctx, const void *X, const void *W, const void *bias, int epilogue, int64_t M,
+                     int64_t N, int64_t K, void *Y, int out_dtype, void *stream) {
+    return run_impl(ctx, X, W, bias, epilogue, M, N, K, Y, out_dtype, stream, false);
+}
+
+proj_status proj_tune(proj_ctx *ctx, const void *X, const void *W, const void *bias, int epilogue, int64_t M,
+                      int64_t N, int64_t K, void *Y, int out_dtype, void *stream) {
+    return run_impl(ctx, X, W, bias, epilogue, M, N, K, Y, out_dtype, stream, true);
+}
+
+proj_status proj_destroy(proj_ctx *ctx) {
+    if (!ctx) return PROJ_ERR_INVALID_ARG;
+    if (ctx->magic == kDead) return PROJ_ERR_DESTROYED;
+    if (ctx->magic != kMagic) return PROJ_ERR_INVALID_ARG;
+    {
+        DeviceGuard g(ctx->device);
+        hipDeviceSynchronize();
+        hipFree(ctx->ws);
+        hipFree(ctx->counters);
+        hipFree(ctx->zeros);
+        if (ctx->flush) hipFree(ctx->flush);
+    }
+    ctx->magic = kDead;
+    delete ctx;
+    return PROJ_OK;
+}
+
+const char *proj_status_string(int s) {
+    switch (s) {
+        case PROJ_OK: return "ok";
+        case PROJ_ERR_INVALID_ARG: return "invalid argument";
+        case PROJ_ERR_UNSUPPORTED: return "unsupported";
+        case PROJ_ERR_HIP: return "HIP runtime error";
+        case PROJ_ERR_NO_MEMORY: return "out of memory or workspace";
+        case PROJ_ERR_NOT_TUNED: return "cannot tune while capturing";
+        case PROJ_ERR_DESTROYED: return "handle already destroyed";
+        default: return "unknown status";
+    }
+}
+
+const char *proj_last_error(const proj_ctx *ctx) {
+    if (!ctx || ctx->magic != kMagic) return "";
+    return ctx->err.c_str();
+}
+
+proj_status proj_get_plan(proj_ctx *ctx, int64_t M, int64_t N, int64_t K, int epi, int out, int aligned16,
+                          char *buf, size_t len) {
+    if (!ctx || ctx->magic != kMagic || !buf || len == 0) return PROJ_ERR_INVALID_ARG;
+    std::lock_guard<std::mutex> lock(ctx->mu);
+    auto it = ctx->plans.find(Key{M, N, K, epi, out, aligned16 ? 1 : 0});
+    if (it == ctx->plans.end()) return PROJ_ERR_INVALID_ARG;
+    char tmp[256];
+    if (it->second.tuned)
+        snprintf(tmp, sizeof tmp, "%s (tuned %.2fus)", it->second.cand.name.c_str(), it->second.us);
+    else
+        snprintf(tmp, sizeof tmp, "%s (default)", it->second.cand.name.c_str());
+    if (std::strlen(tmp) + 1 > len) return PROJ_ERR_INVALID_ARG;
+    std::strcpy(buf, tmp);
+    return PROJ_OK;
+}
+
+int proj_num_candidates(int64_t M, int64_t N, int64_t K, int epi, int out, int aligned16) {
+    if (M <= 0 || N <= 0 || K < 0) return 0;
+    return static_cast<int>(candidates(Key{M, N, K, epi, out, aligned16 ? 1 : 0}).size());
+}
+
+proj_status proj_candidate_name(int64_t M, int64_t N, int64_t K, int epi, int out, int aligned16, int index,
+                                char *buf, size_t len) {
+    if (M <= 0 || N <= 0 || K < 0 || !buf) return PROJ_ERR_INVALID_ARG;
+    std::vector<Candidate> c = candidates(Key{M, N, K, epi, out, aligned16 ? 1 : 0});
+    if (index < 0 || index >= static_cast<int>(c.size())) return PROJ_ERR_INVALID_ARG;
+    if (c[index].name.size() + 1 > len) return PROJ_ERR_INVALID_ARG;
+    std::strcpy(buf, c[index].name.c_str());
+    return PROJ_OK;
+}
+
+proj_status proj_run_candidate(proj_ctx *ctx, int index, const void *X, const void *W, const void *bias, int epi,
+                               int64_t M, int64_t N, int64_t K, void *Y, int out, void *stream) {
+    proj_status s = check_args(ctx, X, W, bias, epi, M, N, K, Y, out);
+    if (s != PROJ_OK || M == 0 || N == 0) return s;
+    const Key k = make_key(X, W, epi, M, N, K, out);
+    std::vector<Candidate> c = candidates(k);
+    if (index < 0 || index >= static_cast<int>(c.size())) {
+        set_err(ctx, "candidate %d out of range (%d)", index, static_cast<int>(c.size()));
+        return PROJ_ERR_INVALID_ARG;
+    }
+    DeviceGuard g(ctx->device);
+    hipError_t e = launch(c[index], make_args(ctx, X, W, bias, epi, M, N, K, Y, out), static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(ctx, "launch", e);
+    return PROJ_OK;
+}
+
+proj_status proj_graph_capture(proj_ctx *ctx, int n_calls, const void *const *X, const void *const *W,
+                               const void *const *bias, void *const *Y, int epi, int64_t M, int64_t N, int64_t K,
+                               int out, void *stream, proj_graph **graph) {
+    if (!ctx || !graph || n_calls <= 0 || !X || !W || !Y || !stream) return PROJ_ERR_INVALID_ARG;
+    if (ctx->magic == kDead) return PROJ_ERR_DESTROYED;
+    if (ctx->magic != kMagic) return PROJ_ERR_INVALID_ARG;
+    *graph = nullptr;
+    for (int i = 0; i < n_calls; ++i) {
+        proj_status s = check_args(ctx, X[i], W[i], bias ? bias[i] : nullptr, epi, M, N, K, Y[i], out);
+        if (s != PROJ_OK) return s;
+    }
+    if (M == 0 || N == 0) return PROJ_ERR_INVALID_ARG;  // nothing to capture
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (capturing(st)) {
+        set_err(ctx, "stream is already capturing");
+        return PROJ_ERR_INVALID_ARG;
+    }
+    DeviceGuard g(ctx->device);
+    // plan first, outside capture (tunes on call 0's buffers)
+    proj_status s = run_impl(ctx, X[0], W[0], bias ? bias[0] : nullptr, epi, M, N, K, Y[0], out, stream, false);
+    if (s != PROJ_OK) return s;
+    hipError_t e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(ctx, "hipStreamSynchronize", e);
+    e = hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) return hip_fail(ctx, "hipStreamBeginCapture", e);
+    for (int i = 0; i < n_calls && s == PROJ_OK; ++i)
+        s = run_impl(ctx, X[i], W[i], bias ? bias[i] : nullptr, epi, M, N, K, Y[i], out, stream, false);
+    hipGraph_t gr = nullptr;
+    e = hipStreamEndCapture(st, &gr);
+    if (s != PROJ_OK) {
+        if (gr) hipGraphDestroy(gr);
+        return s;
+    }
+    if (e != hipSuccess) return hip_fail(ctx, "hipStreamEndCapture", e);
+    hipGraphExec_t ex = nullptr;
+    e = hipGraphInstantiate(&ex, gr, nullptr, nullptr, 0);
+    if (e != hipSuccess) {
+        hipGraphDestroy(gr);
+        return hip_fail(ctx, "hipGraphInstantiate", e);
+    }
+    proj_graph *pg = new (std::nothrow) proj_graph{kMagic, ctx->device, gr, ex};
+    if (!pg) {
+        hipGraphExecDestroy(ex);
+        hipGraphDestroy(gr);
+        return PROJ_ERR_NO_MEMORY;
+    }
+    *graph = pg;
+    return PROJ_OK;
+}
+
+proj_status proj_graph_launch(proj_graph *g, void *stream) {
+    if (!g) return PROJ_ERR_INVALID_ARG;
+    if (g->magic == kDead) return PROJ_ERR_DESTROYED;
+    if (g->magic != kMagic) return PROJ_ERR_INVALID_ARG;
+    DeviceGuard dg(g->device);
+    if (hipGraphLaunch(g->exec, static_cast<hipStream_t>(stream)) != hipSuccess) return PROJ_ERR_HIP;
+    return PROJ_OK;
+}
+
+proj_status proj_graph_destroy(proj_graph *g) {
+    if (!g) return PROJ_ERR_INVALID_ARG;
+    if (g->magic == kDead) return PROJ_ERR_DESTROYED;
+    if (g->magic != kMagic) return PROJ_ERR_INVALID_ARG;
+    DeviceGuard dg(g->device);
+    hipGraphExecDestroy(g->exec);
+    hipGraphDestroy(g->graph);
+    g->magic = kDead;
+    delete g;
+    return PROJ_OK;
+}
+
+}  // extern "C"

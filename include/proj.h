@@ -1,0 +1,174 @@
+/*
+ * proj.h -- C ABI of libproj: the dense projection Y = X . W^T (+ bias)
+ *           (-> GELU tanh) on bf16 inputs with fp32 accumulation, for AMD
+ *           Instinct MI355X (gfx950).
+ *
+ * The operation (worklog "How I made Muse's GPU projections 1.32x faster in
+ * the Open Kernel Challenge", section "The full equation, now with the
+ * letters explained"): for every token row m < M and output feature n < N,
+ *     Y[m, n] = sum over k < K of X[m, k] * W[n, k]
+ * with W stored one output feature per row, so the product is X times the
+ * transpose of W (same page, section "Why the transpose appears").  Inputs
+ * are bf16, products are accumulated in fp32 and only the final value is
+ * rounded to the output type (same page, section "Inputs, products,
+ * accumulators, and outputs are separate choices").  An optional bias is
+ * added to the finished sum (same page, section "What makes it linear?",
+ * affine maps), and an optional GELU is applied after the bias, written
+ * once with the product (page "blackroom" on Devpost, section "How we built
+ * it", the GEMM + GELU epilogue row).  GELU is the tanh form
+ *     0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))).
+ *
+ * Layout, all row-major with unit stride on the last axis:
+ *   X    bf16 [M, K]   token rows            (element m*K + k)
+ *   W    bf16 [N, K]   one row per output    (element n*K + k)
+ *   bias bf16 [N]      (only read when the epilogue has a bias)
+ *   Y    fp32 or bf16 [M, N]                 (element m*N + n)
+ * Pointers are device pointers (hipMalloc'ed or torch CUDA tensors); the
+ * caller owns every buffer and keeps it alive until the enqueued work ends.
+ * X/W/bias may be any alignment; the fast kernels need X and W 16-byte
+ * aligned and K a multiple of 8, and other cases run a slower generic kernel
+ * that gives results within the same tolerance.
+ *
+ * Streams: `stream` is a hipStream_t passed as void* (NULL = the legacy
+ * default stream).  proj_run only enqueues work and returns; it never
+ * synchronises, allocates or reads device memory on the host, so it may be
+ * recorded into a HIP graph (stream capture) -- see "Capture" below.
+ *
+ * Errors: every call returns a proj_status; nothing throws across the ABI.
+ * Arguments are validated before any HIP call.  HIP failures return
+ * PROJ_ERR_HIP and the message is kept in the context (proj_last_error).
+ *
+ * Threading: a context holds one split-K workspace.  Calls that may run at
+ * the same time on the GPU (different streams) must use different contexts,
+ * or the caller must order them.  Host-side, a context may be used from one
+ * thread at a time.
+ */
+#ifndef PROJ_H
+#define PROJ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct proj_ctx proj_ctx;
+typedef struct proj_graph proj_graph;
+
+typedef enum {
+    PROJ_OK = 0,
+    PROJ_ERR_INVALID_ARG = 1,  /* NULL/negative/inconsistent argument */
+    PROJ_ERR_UNSUPPORTED = 2,  /* valid request this library does not do */
+    PROJ_ERR_HIP = 3,          /* a HIP runtime call failed */
+    PROJ_ERR_NO_MEMORY = 4,    /* workspace or allocation too small/failed */
+    PROJ_ERR_NOT_TUNED = 5,    /* tuning requested while the stream captures */
+    PROJ_ERR_DESTROYED = 6     /* handle already destroyed */
+} proj_status;
+
+typedef enum {
+    PROJ_EPI_NONE = 0,           /* Y = X.W^T */
+    PROJ_EPI_BIAS = 1,           /* Y = X.W^T + bias */
+    PROJ_EPI_GELU_TANH = 2,      /* Y = GELU(X.W^T) */
+    PROJ_EPI_BIAS_GELU_TANH = 3  /* Y = GELU(X.W^T + bias) */
+} proj_epilogue;
+
+typedef enum {
+    PROJ_OUT_F32 = 0,  /* fp32 output, round to nearest even from fp32 */
+    PROJ_OUT_BF16 = 1  /* bf16 output, round to nearest even from fp32 */
+} proj_out_dtype;
+
+/* Create a context on HIP device `device`.  Allocates the split-K workspace
+ * and completion counters (zeroed) and a zero page used for masked loads.
+ * Returns PROJ_ERR_INVALID_ARG if ctx is NULL, PROJ_ERR_HIP if the device
+ * cannot be used (e.g. no GPU), PROJ_ERR_UNSUPPORTED if it is not gfx950. */
+proj_status proj_create(proj_ctx **ctx, int device);
+
+/* Enqueue Y = epilogue(X . W^T [+ bias]) on `stream`.
+ *
+ * M, N, K >= 0.  M == 0 or N == 0: nothing to do, PROJ_OK.  K == 0: the
+ * empty sum is 0, so Y = epilogue(bias or 0).  `epilogue` is a
+ * proj_epilogue, `out_dtype` a proj_out_dtype; unknown values give
+ * PROJ_ERR_INVALID_ARG, as do NULL X/W/Y (when the sizes need them) and a
+ * bias epilogue with bias == NULL.
+ *
+ * Plan choice (kernel family, tile shape, split count): on the first call
+ * for a shape key (M, N, K, epilogue, out dtype, alignment) outside stream
+ * capture, every candidate plan is run on the caller's buffers and timed
+ * with HIP events; the fastest is cached and used from then on (this first
+ * call synchronises `stream` and overwrites Y several times; the last run
+ * is the winner's, so Y holds the right result).  Under capture, or with
+ * the environment variable PROJ_TUNE=0, an untimed default plan is used and
+ * cached as "default" (a later uncaptured proj_tune replaces it).
+ *
+ * Capture: proj_run never allocates, synchronises or touches the host
+ * during capture; split-K completion counters reset themselves, so a
+ * captured graph can be replayed any number of times with fresh X.  */
+proj_status proj_run(proj_ctx *ctx, const void *X, const void *W, const void *bias,
+                     int epilogue, int64_t M, int64_t N, int64_t K, void *Y,
+                     int out_dtype, void *stream);
+
+/* Measure the candidates for this shape key now and cache the winner, as
+ * the first uncaptured proj_run does (also re-tunes a key that holds a
+ * default plan).  Returns PROJ_ERR_NOT_TUNED while `stream` is capturing. */
+proj_status proj_tune(proj_ctx *ctx, const void *X, const void *W, const void *bias,
+                      int epilogue, int64_t M, int64_t N, int64_t K, void *Y,
+                      int out_dtype, void *stream);
+
+/* Free the context (synchronises its device first).  The handle must not be
+ * used afterwards; a second destroy of the same pointer is undefined. */
+proj_status proj_destroy(proj_ctx *ctx);
+
+/* Static text for a status code (never NULL). */
+const char *proj_status_string(int status);
+
+/* Last error message recorded in ctx ("" if none; never NULL). */
+const char *proj_last_error(const proj_ctx *ctx);
+
+/* Introspection: the plan cached for a shape key, as text, e.g.
+ * "skinny mt1 nt2 w8 u4 s1 (tuned 18.2us)".  PROJ_ERR_INVALID_ARG if no plan
+ * is cached for that key or buf is too small. */
+proj_status proj_get_plan(proj_ctx *ctx, int64_t M, int64_t N, int64_t K, int epilogue,
+                          int out_dtype, int aligned16, char *buf, size_t buflen);
+
+/* Candidate plans for a shape: how many there are, and their names.  Index
+ * order is stable for a given library build.  Used by tests to run every
+ * kernel variant, and by tools to report the sweep. */
+int proj_num_candidates(int64_t M, int64_t N, int64_t K, int epilogue, int out_dtype,
+                        int aligned16);
+proj_status proj_candidate_name(int64_t M, int64_t N, int64_t K, int epilogue,
+                                int out_dtype, int aligned16, int index, char *buf,
+                                size_t buflen);
+
+/* Enqueue one specific candidate (index as above), bypassing the plan
+ * cache.  Same argument rules as proj_run; PROJ_ERR_INVALID_ARG for an
+ * index out of range, PROJ_ERR_NO_MEMORY if its split workspace does not
+ * fit the context's. */
+proj_status proj_run_candidate(proj_ctx *ctx, int index, const void *X, const void *W,
+                               const void *bias, int epilogue, int64_t M, int64_t N,
+                               int64_t K, void *Y, int out_dtype, void *stream);
+
+/* HIP-graph capture of repeated launches (hot-path row: capture/replay).
+ * Records n_calls proj_run calls, call i using X[i], W[i], bias[i], Y[i]
+ * (bias may be NULL, or bias[i] NULL, when the epilogue has none), all with
+ * one shape, into a graph on `stream`, and instantiates it.  The plan for
+ * the shape is tuned first (outside capture) unless PROJ_TUNE=0.  Replaying
+ * the graph re-runs every call on the same buffers, reading whatever X holds
+ * at replay time. */
+proj_status proj_graph_capture(proj_ctx *ctx, int n_calls, const void *const *X,
+                               const void *const *W, const void *const *bias,
+                               void *const *Y, int epilogue, int64_t M, int64_t N,
+                               int64_t K, int out_dtype, void *stream,
+                               proj_graph **graph);
+
+/* Enqueue one replay of the graph on `stream`. */
+proj_status proj_graph_launch(proj_graph *graph, void *stream);
+
+/* Free the graph (does not synchronise; the caller waits for replays). */
+proj_status proj_graph_destroy(proj_graph *graph);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PROJ_H */

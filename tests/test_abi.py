@@ -1,0 +1,80 @@
+"""The C ABI library loads, exports every symbol include/proj.h declares, and
+its host-side logic (argument checks, status strings, candidate lists) works
+without a GPU.  No compute calls here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dense_linear_projection_amd as dlp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "proj.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(proj_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("proj_create", "proj_run", "proj_destroy"):
+        assert required in names
+    assert sorted(dlp.EXPORTS) == names
+
+
+def test_library_exports_every_declared_symbol():
+    L = dlp.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+        assert ctypes.cast(getattr(L, name), ctypes.c_void_p).value
+
+
+def test_status_strings():
+    assert dlp.proj_status_string(0) == "ok"
+    for s in range(1, 7):
+        assert dlp.proj_status_string(s) not in ("ok", "unknown status")
+    assert dlp.proj_status_string(99) == "unknown status"
+
+
+def test_null_handles_rejected_before_any_hip_call():
+    L = dlp.lib()
+    assert L.proj_run(None, None, None, None, 0, 1, 1, 1, None, 0, None) == dlp.PROJ_ERR_INVALID_ARG
+    assert L.proj_tune(None, None, None, None, 0, 1, 1, 1, None, 0, None) == dlp.PROJ_ERR_INVALID_ARG
+    assert L.proj_destroy(None) == dlp.PROJ_ERR_INVALID_ARG
+    assert L.proj_create(None, 0) == dlp.PROJ_ERR_INVALID_ARG
+    assert L.proj_graph_launch(None, None) == dlp.PROJ_ERR_INVALID_ARG
+    assert L.proj_graph_destroy(None) == dlp.PROJ_ERR_INVALID_ARG
+    assert L.proj_last_error(None) == b""
+
+
+def test_candidate_lists_are_host_logic():
+    # small M: weight-streaming variants with several split counts + GEMMs
+    n = dlp.proj_num_candidates(16, 8192, 8192, dlp.EPI_BIAS, dlp.OUT_BF16)
+    names = [dlp.proj_candidate_name(16, 8192, 8192, dlp.EPI_BIAS, dlp.OUT_BF16, i) for i in range(n)]
+    assert any(x.startswith("skinny_mt1") for x in names)
+    assert any(x.endswith("_s1") for x in names) and any(x.endswith("_s4") for x in names)
+    assert any(x.startswith("gemm_") for x in names)
+    assert len(set(names)) == len(names)          # every candidate is a distinct variant
+    # large M: only the tiled GEMMs
+    big = [dlp.proj_candidate_name(4096, 8192, 8192, 3, 1, i)
+           for i in range(dlp.proj_num_candidates(4096, 8192, 8192, 3, 1))]
+    assert big and all(x.startswith("gemm_") for x in big)
+    # misaligned operands or K % 8 != 0: the generic kernel only
+    assert dlp.proj_num_candidates(16, 64, 100, 0, 0) >= 1
+    assert dlp.proj_candidate_name(16, 64, 64, 0, 0, 0, aligned16=False) == "generic"
+    assert dlp.proj_num_candidates(0, 64, 64, 0, 0) == 0
+    with pytest.raises(dlp.ProjError):
+        dlp.proj_candidate_name(16, 64, 64, 0, 0, 10 ** 6)
+
+
+def test_create_without_gpu_fails_cleanly():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    with pytest.raises(dlp.ProjError) as e:
+        dlp.proj_create(0)
+    assert e.value.status in (dlp.PROJ_ERR_HIP, dlp.PROJ_ERR_INVALID_ARG)

@@ -1,0 +1,97 @@
+"""HIP-graph capture and replay through the C ABI: a replay reads the X it
+finds at replay time (worklog "How I made Muse's GPU projections 1.32x
+faster in the Open Kernel Challenge", section "Fresh graph replay is a
+correctness test too": [2,3] -> [5,8,5], then [3,1] -> [11,5,-3]), and
+split-K counters reset themselves so every replay is right."""
+import numpy as np
+import pytest
+
+import dense_linear_projection_amd as dlp
+import oracle
+import synth
+from oracle import compare
+from tests.gpu_helpers import dev_bf16, host_f64, out_tensor
+
+pytestmark = pytest.mark.gpu
+
+
+def test_replay_follows_fresh_input(ctx):
+    import torch
+    K = 32
+    W = np.zeros((3, K))
+    W[:, :2] = [[4, -1], [1, 2], [-2, 3]]
+    X = np.zeros((1, K))
+    X[0, :2] = [2, 3]
+    Xd = dev_bf16(synth.values_to_bf16(X))
+    Wd = dev_bf16(synth.values_to_bf16(W))
+    Y = out_tensor(1, 3, oracle.OUT_F32)
+    s = torch.cuda.Stream()
+    g = dlp.proj_graph_capture(ctx, [Xd], [Wd], None, [Y], dlp.EPI_NONE, stream=s)
+    try:
+        dlp.proj_graph_launch(g, stream=s)
+        s.synchronize()
+        assert host_f64(Y).tolist() == [[5.0, 8.0, 5.0]]
+        X[0, :2] = [3, 1]
+        Xd.copy_(dev_bf16(synth.values_to_bf16(X)))
+        torch.cuda.synchronize()
+        dlp.proj_graph_launch(g, stream=s)
+        s.synchronize()
+        assert host_f64(Y).tolist() == [[11.0, 5.0, -3.0]]
+    finally:
+        dlp.proj_graph_destroy(g)
+
+
+@pytest.mark.parametrize("shape", [(16, 1024, 8192), (16, 8192, 1024), (300, 640, 512)])
+def test_graph_replays_match_oracle(ctx, shape):
+    """Capture several calls over rotating buffers; replay with eager work
+    and synchronisations in between, new X each time; check every replay."""
+    import torch
+    M, N, K = shape
+    P = 3
+    Ws = [synth.normal_bf16((N, K), 1.0 / np.sqrt(K), 50 + p) for p in range(P)]
+    bs = [synth.normal_bf16((N,), 0.14, 60 + p) for p in range(P)]
+    Xd = [dev_bf16(synth.normal_bf16((M, K), 1.0, 70 + p)) for p in range(P)]
+    Wd = [dev_bf16(w) for w in Ws]
+    bd = [dev_bf16(b) for b in bs]
+    Ys = [out_tensor(M, N, oracle.OUT_BF16) for _ in range(P)]
+    s = torch.cuda.Stream()
+    g = dlp.proj_graph_capture(ctx, Xd, Wd, bd, Ys, dlp.EPI_BIAS, stream=s)
+    try:
+        for rep in range(4):
+            Xs = [synth.normal_bf16((M, K), 1.0, 1000 * rep + p) for p in range(P)]
+            for p in range(P):
+                Xd[p].copy_(dev_bf16(Xs[p]))
+            junk = torch.randn(1 << 20, device="cuda").sum()   # eager work between replays
+            torch.cuda.synchronize()
+            dlp.proj_graph_launch(g, stream=s)
+            s.synchronize()
+            del junk
+            for p in range(P):
+                r, _ = oracle.reference(Xs[p], Ws[p], bs[p], 1, 1)
+                rep_ = compare.check(host_f64(Ys[p]), r)
+                assert rep_["ok"], (rep, p, rep_)
+    finally:
+        dlp.proj_graph_destroy(g)
+    plan = dlp.proj_get_plan(ctx, M, N, K, 1, 1)
+    assert "tuned" in plan, plan
+
+
+def test_capture_without_plan_uses_default(ctx, monkeypatch):
+    """A first-seen shape under capture gets the untimed default plan."""
+    import torch
+    monkeypatch.setenv("PROJ_TUNE", "0")
+    M, N, K = 16, 336, 2048
+    X, W, b = synth.make_inputs(M, N, K, True, 21)
+    Xd, Wd, bd = dev_bf16(X), dev_bf16(W), dev_bf16(b)
+    Y = out_tensor(M, N, oracle.OUT_BF16)
+    s = torch.cuda.Stream()
+    g = dlp.proj_graph_capture(ctx, [Xd], [Wd], [bd], [Y], dlp.EPI_BIAS, stream=s)
+    try:
+        for _ in range(3):
+            dlp.proj_graph_launch(g, stream=s)
+        s.synchronize()
+    finally:
+        dlp.proj_graph_destroy(g)
+    assert "default" in dlp.proj_get_plan(ctx, M, N, K, 1, 1)
+    r, _ = oracle.reference(X, W, b, 1, 1)
+    assert compare.check(host_f64(Y), r)["ok"]

@@ -1,0 +1,157 @@
+"""GPU parity: the HIP path, called through the C ABI, against the fp64 oracle,
+element by element.
+
+* integer-valued inputs make every fp32 partial sum exact in any order, so
+  every kernel variant must match the oracle bit for bit (fp32 and bf16
+  outputs, with bias);
+* random N(0, .) inputs are compared with |u - r| <= 2e-3 + 2e-2 |r|;
+* every candidate plan of a shape is run (not only the tuned winner), at
+  sizes that span several tiles and a ragged tail.
+"""
+import numpy as np
+import pytest
+
+import dense_linear_projection_amd as dlp
+import oracle
+import synth
+from oracle import compare
+from tests.gpu_helpers import dev_bf16, host_f64, out_tensor
+
+pytestmark = pytest.mark.gpu
+
+EPIS = [oracle.EPI_NONE, oracle.EPI_BIAS, oracle.EPI_GELU, oracle.EPI_BIAS_GELU]
+
+
+def run_candidate(ctx, i, Xd, Wd, bd, epi, M, N, K, out):
+    Y = out_tensor(M, N, out)
+    dlp.proj_run_candidate(ctx, i, Xd, Wd, bd if epi & 1 else None, epi, Y, M=M, N=N, K=K)
+    return host_f64(Y)
+
+
+def candidate_names(M, N, K, epi, out, aligned=True):
+    n = dlp.proj_num_candidates(M, N, K, epi, out, aligned)
+    return [dlp.proj_candidate_name(M, N, K, epi, out, i, aligned) for i in range(n)]
+
+
+# shapes that span several tiles of every family and have ragged tails
+INT_SHAPES = [
+    (16, 200, 256),    # N not a multiple of 16
+    (5, 77, 96),       # M < 16
+    (33, 130, 264),    # 3 m-tiles of 16, K % 32 == 8 (partial k-step)
+    (64, 256, 1024),
+    (1, 48, 4104),     # one token row, K % 32 == 8, many k-steps
+    (300, 520, 512),   # large-M family, ragged M and N
+    (257, 129, 128),
+]
+
+
+@pytest.mark.parametrize("shape", INT_SHAPES, ids=lambda s: "M%d_N%d_K%d" % s)
+def test_every_candidate_bit_exact_on_integers(ctx, shape):
+    M, N, K = shape
+    X = synth.integer_bf16((M, K), -8, 8, 10 + M)
+    W = synth.integer_bf16((N, K), -8, 8, 20 + N)
+    b = synth.integer_bf16((N,), -64, 64, 30 + K)
+    Xd, Wd, bd = dev_bf16(X), dev_bf16(W), dev_bf16(b)
+    for epi in (oracle.EPI_NONE, oracle.EPI_BIAS):
+        for out in (oracle.OUT_F32, oracle.OUT_BF16):
+            r, _ = oracle.reference(X, W, b if epi & 1 else None, epi, out)
+            names = candidate_names(M, N, K, epi, out)
+            assert names
+            for i, name in enumerate(names):
+                u = run_candidate(ctx, i, Xd, Wd, bd, epi, M, N, K, out)
+                bad = np.argwhere(u != r)
+                assert bad.size == 0, "%s epi=%d out=%d: first mismatch at %s: %r vs %r" % (
+                    name, epi, out, bad[0], u[tuple(bad[0])], r[tuple(bad[0])])
+
+
+RAND_SHAPES = [(16, 1040, 2048), (64, 200, 1024), (17, 64, 512), (520, 384, 640)]
+
+
+@pytest.mark.parametrize("shape", RAND_SHAPES, ids=lambda s: "M%d_N%d_K%d" % s)
+def test_every_candidate_within_tolerance_random(ctx, shape):
+    M, N, K = shape
+    X, W, b = synth.make_inputs(M, N, K, True, 7)
+    Xd, Wd, bd = dev_bf16(X), dev_bf16(W), dev_bf16(b)
+    for epi in EPIS:
+        out = oracle.OUT_BF16 if epi & 2 else oracle.OUT_F32
+        r, _ = oracle.reference(X, W, b if epi & 1 else None, epi, out)
+        for i, name in enumerate(candidate_names(M, N, K, epi, out)):
+            u = run_candidate(ctx, i, Xd, Wd, bd, epi, M, N, K, out)
+            rep = compare.check(u, r)
+            assert rep["ok"], "%s epi=%d: %s" % (name, epi, rep)
+
+
+@pytest.mark.parametrize("M", [1, 15, 16, 17, 63, 64, 65, 127, 128, 129])
+def test_token_counts_around_tile_edges(ctx, M):
+    """Tuned plan (proj_run) at token counts on both sides of tile edges."""
+    N, K = 272, 1024
+    X, W, b = synth.make_inputs(M, N, K, True, 3)
+    r, _ = oracle.reference(X, W, b, oracle.EPI_BIAS, oracle.OUT_BF16)
+    Y = out_tensor(M, N, oracle.OUT_BF16)
+    dlp.proj_run(ctx, dev_bf16(X), dev_bf16(W), dev_bf16(b), dlp.EPI_BIAS, Y)
+    rep = compare.check(host_f64(Y), r)
+    assert rep["ok"], rep
+
+
+def test_generic_path_unaligned_and_odd_k(ctx):
+    """K % 8 != 0 and a 2-byte-offset X both route to the generic kernel and
+    stay within tolerance."""
+    for (M, N, K, off) in [(7, 33, 100, 0), (16, 64, 256, 1), (3, 5, 7, 1)]:
+        X, W, b = synth.make_inputs(M, N, K, True, 5)
+        r, _ = oracle.reference(X, W, b, oracle.EPI_BIAS_GELU, oracle.OUT_F32)
+        Y = out_tensor(M, N, oracle.OUT_F32)
+        Xd = dev_bf16(X, offset_elems=off)
+        dlp.proj_run(ctx, Xd, dev_bf16(W), dev_bf16(b), dlp.EPI_BIAS_GELU_TANH, Y)
+        rep = compare.check(host_f64(Y), r)
+        assert rep["ok"], (M, N, K, off, rep)
+
+
+def test_degenerate_sizes(ctx):
+    import torch
+    # M == 0 or N == 0: nothing is written
+    Y = out_tensor(4, 4, oracle.OUT_F32, fill=7.0)
+    W = dev_bf16(synth.normal_bf16((4, 32), 1.0, 1))
+    X0 = dev_bf16(np.zeros((0, 32), np.uint16))
+    dlp.proj_run(ctx, X0, W, None, 0, Y, M=0, N=4, K=32)
+    assert torch.all(Y == 7.0).item()
+    # K == 0: the empty sum, so Y = epilogue(bias)
+    b = synth.values_to_bf16([1.5, -2.0, 0.25])
+    Y = out_tensor(2, 3, oracle.OUT_F32)
+    Xe = dev_bf16(np.zeros((2, 0), np.uint16))
+    We = dev_bf16(np.zeros((3, 0), np.uint16))
+    dlp.proj_run(ctx, Xe, We, dev_bf16(b), dlp.EPI_BIAS, Y, M=2, N=3, K=0)
+    assert host_f64(Y).tolist() == [[1.5, -2.0, 0.25]] * 2
+    dlp.proj_run(ctx, Xe, We, dev_bf16(b), dlp.EPI_BIAS_GELU_TANH, Y, M=2, N=3, K=0)
+    r = oracle.round_out(oracle.gelu_tanh(np.array([1.5, -2.0, 0.25])), oracle.OUT_F32)
+    assert compare.check(host_f64(Y)[0], r.astype(np.float64))["ok"]
+
+
+def test_invalid_arguments_are_rejected(ctx):
+    W = dev_bf16(synth.normal_bf16((4, 32), 1.0, 1))
+    X = dev_bf16(synth.normal_bf16((2, 32), 1.0, 2))
+    Y = out_tensor(2, 4, oracle.OUT_F32)
+    L = dlp.lib()
+    args = lambda epi=0, M=2, out=0, bias=None, Yp=Y.data_ptr(): (
+        ctx, X.data_ptr(), W.data_ptr(), bias, epi, M, 4, 32, Yp, out, None)
+    assert L.proj_run(*args(M=-1)) == dlp.PROJ_ERR_INVALID_ARG
+    assert L.proj_run(*args(epi=7)) == dlp.PROJ_ERR_INVALID_ARG
+    assert L.proj_run(*args(out=5)) == dlp.PROJ_ERR_INVALID_ARG
+    assert L.proj_run(*args(epi=1)) == dlp.PROJ_ERR_INVALID_ARG        # bias missing
+    assert L.proj_run(*args(Yp=None)) == dlp.PROJ_ERR_INVALID_ARG
+    assert L.proj_run(*args(Yp=Y.data_ptr() + 2)) == dlp.PROJ_ERR_INVALID_ARG  # fp32 Y misaligned
+    assert b"bias" in L.proj_last_error(ctx) or L.proj_last_error(ctx)
+
+
+def test_nonfinite_inputs_propagate(ctx):
+    M, N, K = 16, 64, 512
+    X, W, _ = synth.make_inputs(M, N, K, False, 9)
+    X = X.copy()
+    X[3, 100] = 0x7FC0           # NaN
+    X[5, 7] = 0x7F80             # +inf
+    Y = out_tensor(M, N, oracle.OUT_F32, fill=0.0)
+    dlp.proj_run(ctx, dev_bf16(X), dev_bf16(W), None, 0, Y)
+    u = host_f64(Y)
+    assert np.isnan(u[3]).all()
+    assert (~np.isfinite(u[5])).all()
+    others = [m for m in range(M) if m not in (3, 5)]
+    assert np.isfinite(u[others]).all()
