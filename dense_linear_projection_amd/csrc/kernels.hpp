@@ -11,10 +11,22 @@ struct SkinnyVariant {
     const char *family;
     int mt, nt, waves, unroll;
     bool nontemporal;
+    bool rotate;  // per-workgroup rotation of the K start
     hipError_t (*launch)(const Args &, int splits, hipStream_t);
 };
 extern const SkinnyVariant kSkinnyVariants[];
 extern const int kNumSkinnyVariants;
+
+// Weight-streaming kernel staged through an LDS ring (stream.hip); with
+// splits > 1 a second kernel adds the partials and applies the epilogue.
+struct StreamVariant {
+    const char *family;
+    int mt, nt, waves, kc, depth;
+    hipError_t (*launch)(const Args &, int splits, hipStream_t);
+    hipError_t (*prepare)();  // one-time function attributes (LDS size)
+};
+extern const StreamVariant kStreamVariants[];
+extern const int kNumStreamVariants;
 
 // LDS-pipelined MFMA GEMM for large M (gemm.hip).
 struct GemmVariant {
@@ -28,5 +40,9 @@ extern const int kNumGemmVariants;
 
 // Any shape, any alignment (generic.hip).
 hipError_t launch_generic(const Args &a, hipStream_t st);
+
+// Read `bytes` of `buf` to evict other data from the caches (generic.hip);
+// `sink` needs room for 256 unsigned.
+hipError_t launch_flush(const void *buf, size_t bytes, unsigned *sink, hipStream_t st);
 
 }  // namespace proj

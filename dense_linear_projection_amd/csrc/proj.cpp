@@ -47,7 +47,7 @@ struct Key {
     }
 };
 
-enum Kind { KIND_SKINNY = 0, KIND_GEMM = 1, KIND_GENERIC = 2 };
+enum Kind { KIND_SKINNY = 0, KIND_GEMM = 1, KIND_GENERIC = 2, KIND_STREAM = 3 };
 
 struct Candidate {
     Kind kind;
@@ -135,8 +135,14 @@ size_t skinny_ws_bytes(const SkinnyVariant &v, int64_t N, int S) {
 
 std::string skinny_name(const SkinnyVariant &v, int S) {
     char b[96];
-    snprintf(b, sizeof b, "skinny_mt%d_nt%d_w%d_u%d%s_s%d", v.mt, v.nt, v.waves, v.unroll,
-             v.nontemporal ? "_ntl" : "", S);
+    snprintf(b, sizeof b, "skinny_mt%d_nt%d_w%d_u%d%s%s_s%d", v.mt, v.nt, v.waves, v.unroll,
+             v.nontemporal ? "_ntl" : "", v.rotate ? "_rot" : "", S);
+    return b;
+}
+
+std::string stream_name(const StreamVariant &v, int S) {
+    char b[96];
+    snprintf(b, sizeof b, "stream_mt%d_nt%d_w%d_k%d_d%d_s%d", v.mt, v.nt, v.waves, v.kc, v.depth, S);
     return b;
 }
 
@@ -167,6 +173,20 @@ std::vector<Candidate> candidates(const Key &k) {
                 }
             }
         }
+        if (mt > 0) {
+            for (int i = 0; i < kNumStreamVariants; ++i) {
+                const StreamVariant &v = kStreamVariants[i];
+                if (v.mt != mt) continue;
+                const int64_t stages = (k.K + v.kc - 1) / v.kc;
+                const int64_t tiles = (k.N + 16 * v.nt - 1) / (16 * v.nt);
+                for (int S : {1, 2, 4, 8}) {
+                    if (S > 1 && S > stages) continue;
+                    if (S > 1 && static_cast<size_t>(S) * k.M * k.N * sizeof(float) > kWorkspaceBytes) continue;
+                    if (tiles * S > 0x7fffffff) continue;
+                    out.push_back({KIND_STREAM, i, S, stream_name(v, S)});
+                }
+            }
+        }
         for (int i = 0; i < kNumGemmVariants; ++i) {
             const GemmVariant &v = kGemmVariants[i];
             if (k.K % v.bk != 0) continue;
@@ -190,7 +210,7 @@ Candidate default_candidate(const Key &k) {
         for (const Candidate &x : c) {
             if (x.kind != KIND_SKINNY) continue;
             const SkinnyVariant &v = kSkinnyVariants[x.variant];
-            if (v.nt != 1 || v.waves != 8 || v.unroll != 4 || v.nontemporal) continue;
+            if (v.nt != 1 || v.waves != 8 || v.unroll != 4 || v.nontemporal || v.rotate) continue;
             if (skinny_tiles(v, k.N) * x.splits >= 256 || x.splits == 16) return x;
         }
     }
@@ -222,6 +242,7 @@ hipError_t launch(const Candidate &cand, const Args &a, hipStream_t st) {
     switch (cand.kind) {
         case KIND_SKINNY: return kSkinnyVariants[cand.variant].launch(a, cand.splits, st);
         case KIND_GEMM: return kGemmVariants[cand.variant].launch(a, st);
+        case KIND_STREAM: return kStreamVariants[cand.variant].launch(a, cand.splits, st);
         default: return launch_generic(a, st);
     }
 }
@@ -289,15 +310,16 @@ proj_status tune(proj_ctx *c, const Key &k, const Args &a, hipStream_t st, Plan 
     const size_t bytes = static_cast<size_t>(2 * (k.M + k.N) * k.K);
     const bool flush = bytes < kFlushBytes;
     if (flush && !c->flush) {
-        if (hipMalloc(&c->flush, kFlushBytes) != hipSuccess) c->flush = nullptr;
+        if (hipMalloc(&c->flush, kFlushBytes + 1024) != hipSuccess) c->flush = nullptr;
     }
+    unsigned *sink = c->flush ? reinterpret_cast<unsigned *>(static_cast<char *>(c->flush) + kFlushBytes) : nullptr;
     hipEvent_t e0, e1;
     if (hipEventCreate(&e0) != hipSuccess) return hip_fail(c, "hipEventCreate", hipGetLastError());
     if (hipEventCreate(&e1) != hipSuccess) {
         hipEventDestroy(e0);
         return hip_fail(c, "hipEventCreate", hipGetLastError());
     }
-    const int reps = 5;
+    const int reps = 7;
     float best = 1e30f;
     int best_i = -1;
     for (size_t i = 0; i < cands.size(); ++i) {
@@ -308,7 +330,7 @@ proj_status tune(proj_ctx *c, const Key &k, const Args &a, hipStream_t st, Plan 
         std::vector<float> t;
         bool ok = true;
         for (int r = 0; r < reps && ok; ++r) {
-            if (flush && c->flush) hipMemsetAsync(c->flush, r & 0xff, kFlushBytes, st);
+            if (flush && c->flush) launch_flush(c->flush, kFlushBytes, sink, st);
             hipEventRecord(e0, st);
             ok = launch(cands[i], a, st) == hipSuccess;
             hipEventRecord(e1, st);
@@ -403,6 +425,7 @@ proj_status proj_create(proj_ctx **out, int device) {
               hipMemset(c->counters, 0, kCounters * sizeof(unsigned)) == hipSuccess &&
               hipMemset(c->zeros, 0, kZeroBytes) == hipSuccess;
     for (int i = 0; ok && i < kNumGemmVariants; ++i) ok = kGemmVariants[i].prepare() == hipSuccess;
+    for (int i = 0; ok && i < kNumStreamVariants; ++i) ok = kStreamVariants[i].prepare() == hipSuccess;
     ok = ok && hipDeviceSynchronize() == hipSuccess;
     if (!ok) {
         hipFree(c->ws);

@@ -42,7 +42,7 @@
 
 namespace proj {
 
-template <int MT, int NT, int WAVES, int U, bool NTL>
+template <int MT, int NT, int WAVES, int U, bool NTL, bool ROT>
 __global__ __launch_bounds__(WAVES * 64) void skinny_kernel(Args a, int S) {
     constexpr int E = MT * NT * 256;  // fp32 outputs per workgroup tile
     __shared__ float red[WAVES * E];
@@ -76,8 +76,18 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_kernel(Args a, int S) {
     const int64_t Tfull = K / 32;
     const int64_t tb = (T * split) / S, te = (T * (split + 1)) / S;
     const int64_t tfe = te < Tfull ? te : Tfull;  // end of full steps in range
-    const int64_t t0 = tb + wave;
-    const int64_t nj = tfe > t0 ? (tfe - t0 + WAVES - 1) / WAVES : 0;
+    const int64_t nfull = tfe > tb ? tfe - tb : 0;  // full k-steps of this split
+    // Position p of the split's full steps is k-step tb + (p + rot) mod nfull.
+    // With ROT, workgroups start at different k so that, at any moment, the
+    // machine's loads are spread over the whole K extent of W instead of all
+    // hitting the same column offset of every (power-of-two strided) row.
+    const int64_t rot = (ROT && nfull > 0) ? (static_cast<int64_t>(tile) * 97) % nfull : 0;
+    const int64_t nj = nfull > wave ? (nfull - wave + WAVES - 1) / WAVES : 0;
+    auto step = [&](int64_t j) -> int64_t {
+        int64_t p = wave + j * WAVES + rot;
+        if (p >= nfull) p -= nfull;
+        return tb + p;
+    };
 
     f32x4 acc[MT][NT];
 #pragma unroll
@@ -98,7 +108,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_kernel(Args a, int S) {
     if (nb > 0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            int64_t t = t0 + static_cast<int64_t>(u) * WAVES;
+            int64_t t = step(u);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) wc[u][nt] = ldw(nt, t);
 #pragma unroll
@@ -111,7 +121,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_kernel(Args a, int S) {
         if (b + 1 < nb) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                int64_t t = t0 + ((b + 1) * U + u) * WAVES;
+                int64_t t = step((b + 1) * U + u);
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) wn[u][nt] = ldw(nt, t);
 #pragma unroll
@@ -135,7 +145,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_kernel(Args a, int S) {
     }
     // leftover full steps
     for (int64_t j = nb * U; j < nj; ++j) {
-        int64_t t = t0 + j * WAVES;
+        int64_t t = step(j);
         bf16x8 w1[NT], x1[MT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) w1[nt] = ldw(nt, t);
@@ -240,27 +250,34 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_kernel(Args a, int S) {
 // One list drives both compilation passes: the device pass instantiates the
 // kernels, the host pass builds the launch table.  Variants that would spill
 // registers at their occupancy are left out.
-#define PROJ_SKINNY_VARIANTS(X)                                                                  \
-    X(1, 1, 4, 4, false) X(1, 1, 8, 4, false) X(1, 1, 8, 8, false) X(1, 1, 16, 4, false)          \
-    X(1, 2, 8, 4, false) X(1, 2, 16, 2, false) X(1, 4, 8, 2, false) X(1, 1, 8, 4, true)           \
-    X(1, 2, 8, 4, true) X(1, 1, 16, 4, true) X(2, 1, 8, 4, false) X(2, 2, 8, 4, false)            \
-    X(2, 2, 16, 2, false) X(4, 1, 8, 4, false) X(4, 2, 8, 2, false) X(4, 4, 4, 2, false)
+#define PROJ_SKINNY_VARIANTS(X)                                                                            \
+    X(1, 1, 4, 4, false, false) X(1, 1, 8, 4, false, false) X(1, 1, 8, 8, false, false)                     \
+    X(1, 1, 16, 4, false, false) X(1, 2, 8, 4, false, false) X(1, 2, 16, 2, false, false)                   \
+    X(1, 4, 8, 2, false, false) X(1, 1, 8, 4, true, false) X(1, 2, 16, 2, true, false)                      \
+    X(1, 1, 8, 4, false, true) X(1, 1, 8, 8, false, true) X(1, 1, 16, 4, false, true)                        \
+    X(1, 2, 8, 4, false, true) X(1, 2, 16, 2, false, true) X(1, 1, 8, 4, true, true)                         \
+    X(1, 2, 16, 2, true, true) X(2, 1, 8, 4, false, false) X(2, 2, 8, 4, false, false)                       \
+    X(2, 2, 16, 2, false, false) X(2, 2, 16, 2, false, true) X(4, 1, 8, 4, false, false)                    \
+    X(4, 2, 8, 2, false, false) X(4, 4, 4, 2, false, false) X(4, 2, 8, 2, false, true)                      \
+    X(4, 4, 4, 2, false, true)
 
-#define PROJ_SKINNY_INST(MT, NT, WV, U, NTL) template __global__ void skinny_kernel<MT, NT, WV, U, NTL>(Args, int);
+#define PROJ_SKINNY_INST(MT, NT, WV, U, NTL, ROT) \
+    template __global__ void skinny_kernel<MT, NT, WV, U, NTL, ROT>(Args, int);
 PROJ_SKINNY_VARIANTS(PROJ_SKINNY_INST)
 
 #ifndef __HIP_DEVICE_COMPILE__
-template <int MT, int NT, int WAVES, int U, bool NTL>
+template <int MT, int NT, int WAVES, int U, bool NTL, bool ROT>
 static hipError_t launch_skinny(const Args &a, int S, hipStream_t st) {
     const int64_t tiles = (a.N + 16 * NT - 1) / (16 * NT);
     const int64_t grid = tiles * S;
     if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((skinny_kernel<MT, NT, WAVES, U, NTL>), dim3(static_cast<unsigned>(grid)),
+    hipLaunchKernelGGL((skinny_kernel<MT, NT, WAVES, U, NTL, ROT>), dim3(static_cast<unsigned>(grid)),
                        dim3(WAVES * 64), 0, st, a, S);
     return hipGetLastError();
 }
 
-#define PROJ_SKINNY_ENTRY(MT, NT, WV, U, NTL) {"skinny", MT, NT, WV, U, NTL, &launch_skinny<MT, NT, WV, U, NTL>},
+#define PROJ_SKINNY_ENTRY(MT, NT, WV, U, NTL, ROT) \
+    {"skinny", MT, NT, WV, U, NTL, ROT, &launch_skinny<MT, NT, WV, U, NTL, ROT>},
 const SkinnyVariant kSkinnyVariants[] = {PROJ_SKINNY_VARIANTS(PROJ_SKINNY_ENTRY)};
 const int kNumSkinnyVariants = sizeof(kSkinnyVariants) / sizeof(kSkinnyVariants[0]);
 #endif

@@ -1,0 +1,261 @@
+// stream.hip -- weight-streaming projection for few token rows (M <= 64),
+// staged through an LDS ring filled by global->LDS DMA.
+//
+// At small M each weight is used by only M token rows, so the projection is
+// bound by reading W once (worklog "How I made Muse's GPU projections 1.32x
+// faster in the Open Kernel Challenge", section "A rough way to ask how much
+// room was left": M flops per weight byte).  What matters is keeping enough
+// W bytes in flight on every CU, reading them in long contiguous runs, and
+// doing the little arithmetic on the side.
+//
+// Decomposition:
+//   * a workgroup owns 16*NT output features (W rows) and one of S
+//     contiguous ranges of K, cut at KC-element stage boundaries as evenly
+//     as integers allow (stages floor(s*T/S) .. floor((s+1)*T/S)); with S > 1
+//     each range writes an fp32 partial tile and a second kernel adds the S
+//     partials in split order and applies the epilogue (the worklog's
+//     split-K with a partial workspace, section "My first useful win: split
+//     up the sum");
+//   * a stage is W[16*NT rows][KC] plus X[16*MT rows][KC], copied into one
+//     slot of a D-deep LDS ring with global_load_lds_dwordx4: one wave
+//     instruction moves 1 KB made of whole rows' KC-element runs, so every
+//     row segment read from HBM is 2*KC contiguous bytes;
+//   * the waves of the workgroup share the copies, wait for their own
+//     copies with an explicit vmcnt, and meet at one barrier per stage; the
+//     barrier publishes stage i and frees the slot of stage i-1, which is
+//     refilled with stage i+D-1 right away, so D-1 stages stay in flight;
+//   * in a stage, wave w multiplies k-steps w, w+WAVES, ... (32 k each) for
+//     all of its tile with v_mfma_f32_16x16x32_bf16 (A = 16 token rows x 32 k
+//     of X, B = 32 k x 16 features of W, both read from LDS), accumulating
+//     fp32; the waves' partial tiles are summed through LDS at the end;
+//   * LDS rows hold 16-byte chunks at position chunk ^ (row & 15), so the 16
+//     rows read by one fragment load fall on distinct banks; the DMA writes
+//     lane i to position i, so the XOR picks each lane's global source;
+//   * workgroups walk their stages starting at a tile-dependent rotation, so
+//     at any moment the machine's reads are spread over all of K rather than
+//     all hitting the same column offset of every power-of-two-strided row.
+// Chunks past K or rows past M / N read the zero page (no load leaves the
+// caller's buffers); rows past M / N are not stored.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace proj {
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// wait until at most `ahead` stages of PERW copies are still in flight
+template <int PERW, int MAXAHEAD>
+__device__ __forceinline__ void wait_stages(int ahead) {
+    if constexpr (MAXAHEAD <= 0) {
+        wait_vm<0>();
+    } else {
+        if (ahead >= MAXAHEAD)
+            wait_vm<PERW * MAXAHEAD>();
+        else
+            wait_stages<PERW, MAXAHEAD - 1>(ahead);
+    }
+}
+
+template <int MT, int NT, int WAVES, int KC, int D>
+struct StreamCfg {
+    static constexpr int NR = 16 * NT;               // W rows per workgroup
+    static constexpr int MR = 16 * MT;               // X rows (padded to 16s)
+    static constexpr int ROWB = KC * 2;              // bytes per row per stage
+    static constexpr int CPR = ROWB / 16;            // 16-byte chunks per row
+    static constexpr int RPI = 1024 / ROWB;          // rows per DMA instruction
+    static constexpr int STAGE = (NR + MR) * ROWB;   // bytes per stage
+    static constexpr int NINSTR = STAGE / 1024;
+    static constexpr int PERW = NINSTR / WAVES;      // DMA instructions per wave per stage
+    static constexpr int KS = KC / 32;               // k-steps per stage
+    static constexpr int RED = WAVES * MT * NT * 1024;  // reduction scratch bytes
+    static constexpr int LDS = (D * STAGE > RED) ? D * STAGE : RED;
+    static_assert(ROWB <= 1024 && 1024 % ROWB == 0, "a DMA block holds whole row runs");
+    static_assert(CPR >= 16, "swizzle spans 16 chunks");
+    static_assert(NINSTR % WAVES == 0, "copies divide evenly over the waves");
+    static_assert(KS % WAVES == 0 || WAVES % KS == 0, "k-steps divide over the waves");
+    static_assert(KS >= WAVES, "every wave gets a k-step per stage");
+    static_assert(PERW * (D - 2) <= 63, "vmcnt range");
+    static_assert(D >= 2, "ring depth");
+};
+
+template <int MT, int NT, int WAVES, int KC, int D>
+__global__ __launch_bounds__(WAVES * 64) void stream_kernel(Args a, int S) {
+    using C = StreamCfg<MT, NT, WAVES, KC, D>;
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tile = blockIdx.x / S, split = blockIdx.x % S;
+    const int64_t K = a.K, M = a.M, N = a.N;
+    const int64_t n0 = static_cast<int64_t>(tile) * C::NR;
+
+    // stage range of this split, and the rotated walk over it
+    const int64_t T = (K + KC - 1) / KC;
+    const int64_t sb = (T * split) / S, se = (T * (split + 1)) / S;
+    const int nst = static_cast<int>(se - sb);
+    const int rot = nst > 0 ? static_cast<int>((static_cast<int64_t>(tile) * 7) % nst) : 0;
+    auto stage_k0 = [&](int i) -> int64_t {
+        int q = i + rot;
+        if (q >= nst) q -= nst;
+        return (sb + q) * KC;
+    };
+
+    // per-lane DMA sources: instruction j of this wave fills block
+    // b = wave + j*WAVES of the stage, rows b*RPI + lane/CPR, position
+    // lane%CPR, which holds chunk (lane%CPR) ^ (row & 15).
+    const uint16_t *src[C::PERW];
+    int kofs[C::PERW];
+#pragma unroll
+    for (int j = 0; j < C::PERW; ++j) {
+        const int row = (wave + j * WAVES) * C::RPI + lane / C::CPR;
+        const int chunk = (lane % C::CPR) ^ (row & 15);
+        kofs[j] = chunk * 8;
+        if (row < C::NR) {
+            const int64_t n = n0 + row;
+            src[j] = n < N ? a.W + n * K + chunk * 8 : nullptr;
+        } else {
+            const int64_t m = row - C::NR;
+            src[j] = m < M ? a.X + m * K + chunk * 8 : nullptr;
+        }
+    }
+    auto issue = [&](int i) {
+        char *slot = lds + (i % D) * C::STAGE;
+        const int64_t k0 = i < nst ? stage_k0(i) : 0;
+#pragma unroll
+        for (int j = 0; j < C::PERW; ++j) {
+            const bool ok = i < nst && src[j] != nullptr && k0 + kofs[j] < K;
+            dma16(ok ? static_cast<const void *>(src[j] + k0) : static_cast<const void *>(a.zeros),
+                  slot + (wave + j * WAVES) * 1024);
+        }
+    };
+
+    f32x4 acc[MT][NT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int fr = lane & 15, fg = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < D - 1; ++i) issue(i);
+
+    for (int i = 0; i < nst; ++i) {
+        // this wave's copies of stage i are done once at most
+        // min(D-2, nst-1-i) later stages are still in flight
+        wait_stages<C::PERW, D - 2>(nst - 1 - i);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (i + D - 1 < nst) issue(i + D - 1);
+        const char *slot = lds + (i % D) * C::STAGE;
+#pragma unroll
+        for (int kk = wave % C::KS; kk < C::KS; kk += WAVES) {
+            const int c = kk * 4 + fg;
+            bf16x8 xf[MT], wf[NT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const int row = C::NR + mt * 16 + fr;
+                xf[mt] = *reinterpret_cast<const bf16x8 *>(slot + row * C::ROWB + ((c ^ (row & 15)) << 4));
+            }
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const int row = nt * 16 + fr;
+                wf[nt] = *reinterpret_cast<const bf16x8 *>(slot + row * C::ROWB + ((c ^ (row & 15)) << 4));
+            }
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma16x16x32(xf[mt], wf[nt], acc[mt][nt]);
+        }
+    }
+    wait_vm<0>();
+    __syncthreads();
+
+    // ---- sum the waves' partial tiles: red[wave][tile][i][lane]
+    float *red = reinterpret_cast<float *>(lds);
+    constexpr int E = MT * NT * 256;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[wave * E + (mt * NT + nt) * 256 + r * 64 + lane] = acc[mt][nt][r];
+    __syncthreads();
+
+    const uint16_t *bias = a.bias;
+#pragma unroll
+    for (int q = 0; q < (E + WAVES * 64 - 1) / (WAVES * 64); ++q) {
+        const int e = tid + q * WAVES * 64;
+        if (e >= E) break;
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) s += red[w * E + e];
+        // MFMA output layout: lane holds column lane%16, rows 4*(lane/16) + r
+        const int tl = e >> 8, r = (e >> 6) & 3, ln = e & 63;
+        const int64_t m = (tl / NT) * 16 + 4 * (ln >> 4) + r;
+        const int64_t n = n0 + (tl % NT) * 16 + (ln & 15);
+        if (m >= M || n >= N) continue;
+        if (S == 1) {
+            const float b = (a.epi & 1) ? bf16_bits_to_f32(bias[n]) : 0.f;
+            store_out(a.Y, a.out, m * N + n, apply_epilogue(s, a.epi, b));
+        } else {
+            a.ws[(static_cast<int64_t>(split) * M + m) * N + n] = s;
+        }
+    }
+}
+
+// Second pass of split-K: Y[m, n] = epilogue(sum over s of ws[s, m, n]),
+// summed in split order.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(Args a, int S) {
+    const int64_t MN = a.M * a.N;
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (idx >= MN) return;
+    float s = 0.f;
+    for (int sp = 0; sp < S; ++sp) s += a.ws[sp * MN + idx];
+    const int64_t n = idx % a.N;
+    const float b = (a.epi & 1) ? bf16_bits_to_f32(a.bias[n]) : 0.f;
+    store_out(a.Y, a.out, idx, apply_epilogue(s, a.epi, b));
+}
+
+// ---------------------------------------------------------------- registry
+#define PROJ_STREAM_VARIANTS(X)                                                                  \
+    X(1, 1, 8, 256, 4) X(1, 2, 8, 256, 4) X(1, 2, 8, 256, 3) X(1, 1, 8, 512, 3)                  \
+    X(1, 2, 4, 256, 4) X(1, 4, 8, 256, 3) X(1, 2, 8, 512, 3) X(2, 2, 8, 256, 4)                  \
+    X(4, 2, 8, 256, 3) X(4, 4, 8, 256, 2) X(4, 4, 4, 128, 4) X(4, 2, 4, 128, 4) X(4, 7, 4, 128, 3)
+
+#define PROJ_STREAM_INST(MT, NT, WV, KC, D) \
+    template __global__ void stream_kernel<MT, NT, WV, KC, D>(Args, int);
+PROJ_STREAM_VARIANTS(PROJ_STREAM_INST)
+
+#ifndef __HIP_DEVICE_COMPILE__
+template <int MT, int NT, int WV, int KC, int D>
+static hipError_t prepare_stream() {
+    auto fn = stream_kernel<MT, NT, WV, KC, D>;
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               StreamCfg<MT, NT, WV, KC, D>::LDS);
+}
+
+template <int MT, int NT, int WV, int KC, int D>
+static hipError_t launch_stream(const Args &a, int S, hipStream_t st) {
+    const int64_t tiles = (a.N + 16 * NT - 1) / (16 * NT);
+    const int64_t grid = tiles * S;
+    if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    constexpr int lds_bytes = StreamCfg<MT, NT, WV, KC, D>::LDS;
+    hipLaunchKernelGGL((stream_kernel<MT, NT, WV, KC, D>), dim3(static_cast<unsigned>(grid)), dim3(WV * 64),
+                       lds_bytes, st, a, S);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || S == 1) return e;
+    const int64_t blocks = (a.M * a.N + 255) / 256;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a, S);
+    return hipGetLastError();
+}
+
+#define PROJ_STREAM_ENTRY(MT, NT, WV, KC, D) \
+    {"stream", MT, NT, WV, KC, D, &launch_stream<MT, NT, WV, KC, D>, &prepare_stream<MT, NT, WV, KC, D>},
+const StreamVariant kStreamVariants[] = {PROJ_STREAM_VARIANTS(PROJ_STREAM_ENTRY)};
+const int kNumStreamVariants = sizeof(kStreamVariants) / sizeof(kStreamVariants[0]);
+#endif
+
+}  // namespace proj
