@@ -37,27 +37,115 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 LLC_BYTES = 256 << 20          # last-level (Infinity) cache
 
 
-def kernel_sources_hash() -> str:
+# the source files that define each kernel family (the counters of a family
+# are stale once any of its files changes)
+FAMILY_SOURCES = {
+    "stream_kernel": ["stream.hip", "common.hpp"],
+    "gemm_kernel": ["gemm.hip", "common.hpp"],
+    "gemm_pipe_kernel": ["gemm.hip", "common.hpp"],
+}
+
+
+def kernel_sources_hash(family: str) -> str:
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "dense_linear_projection_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
-            h.update(os.path.basename(p).encode())
+    for name in FAMILY_SOURCES[family]:
+        with open(os.path.join(ROOT, "dense_linear_projection_amd", "csrc", name), "rb") as f:
+            h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload_name: str, launches_per_step: int):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they
-    were taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", "counters_%s.json" % workload_name)
+def family_of(kernel_name: str) -> str:
+    for fam in FAMILY_SOURCES:
+        if kernel_name.startswith(fam.split("_kernel")[0].replace("_", "")) or fam in kernel_name:
+            return fam
+    raise ValueError("unknown kernel family for %r" % kernel_name)
+
+
+def counters_path(workload_name: str) -> str:
+    return os.path.join(ROOT, "profiles", "counters_%s.json" % workload_name)
+
+
+def load_traffic(workload_name: str):
+    """HBM bytes per launch of the projection kernel, from committed
+    rocprofv3 counter runs (FETCH_SIZE and WRITE_SIZE, each scaled by what
+    the same counter reads for a plain copy of known size), if they were
+    taken on the current kernel sources; else None."""
+    path = counters_path(workload_name)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         c = json.load(f)
-    if c.get("src_hash") != kernel_sources_hash():
+    if c.get("src_hash") != kernel_sources_hash(c["family"]):
         return None
-    kib = (c["fetch_kib_per_dispatch"] + c["write_kib_per_dispatch"]) * c["copy_scale"]
-    return kib * 1024.0 * launches_per_step / launches_per_step
+    return round(c["fetch_kib_per_dispatch"] * 1024 * c["fetch_scale"]
+                 + c["write_kib_per_dispatch"] * 1024 * c["write_scale"], 1)
+
+
+def _pmc_per_dispatch(run_dir: str, counter: str, name_part: str, skip_first: int = 0):
+    """Mean of one counter over the dispatches of kernels whose name holds
+    name_part, from a rocprofv3 --pmc CSV output directory."""
+    import csv
+    vals = {}
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if name_part in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                    key = (path, r["Dispatch_Id"])
+                    vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+    xs = [v for _, v in sorted(vals.items(), key=lambda kv: int(kv[0][1]))][skip_first:]
+    if not xs:
+        raise SystemExit("no %s samples for kernels matching %r in %s" % (counter, name_part, run_dir))
+    return sum(xs) / len(xs), len(xs)
+
+
+def ingest_counters(args) -> int:
+    """Write profiles/counters_<workload>.json from four rocprofv3 --pmc runs:
+    FETCH_SIZE and WRITE_SIZE of this bench, and of --copy-calibration."""
+    import synth
+    w = synth.WORKLOADS[args.workload]
+    kern = args.kernel_name
+    fetch, nf = _pmc_per_dispatch(args.ingest[0], "FETCH_SIZE", kern, skip_first=0)
+    write, nw = _pmc_per_dispatch(args.ingest[1], "WRITE_SIZE", kern, skip_first=0)
+    cfetch, _ = _pmc_per_dispatch(args.ingest[2], "FETCH_SIZE", "copy")
+    cwrite, _ = _pmc_per_dispatch(args.ingest[3], "WRITE_SIZE", "copy")
+    copy_bytes = COPY_BYTES
+    out = {
+        "workload": w.name,
+        "kernel_name_part": kern,
+        "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
+        "dispatches": [nf, nw],
+        "copy_bytes": copy_bytes,
+        "copy_fetch_kib": cfetch, "copy_write_kib": cwrite,
+        "fetch_scale": copy_bytes / (cfetch * 1024), "write_scale": copy_bytes / (cwrite * 1024),
+        "alg_bytes_per_launch": w.alg_bytes(),
+        "family": family_of(kern),
+        "src_files": FAMILY_SOURCES[family_of(kern)],
+        "src_hash": kernel_sources_hash(family_of(kern)),
+    }
+    out["traffic_bytes_per_launch"] = (out["fetch_kib_per_dispatch"] * 1024 * out["fetch_scale"]
+                                       + out["write_kib_per_dispatch"] * 1024 * out["write_scale"])
+    with open(counters_path(w.name), "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+    return 0
+
+
+COPY_BYTES = 256 << 20
+
+
+def copy_calibration() -> int:
+    """A plain device-to-device copy of COPY_BYTES, repeated, for scaling
+    the FETCH_SIZE / WRITE_SIZE counters (run under rocprofv3 --pmc)."""
+    import torch
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print("copied %d bytes 10 times" % COPY_BYTES)
+    return 0
 
 
 def cpu_baseline(w, X, W, b, min_seconds: float):
@@ -99,7 +187,16 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--graph-calls", type=int, default=0, help="calls per captured graph (0: auto)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain copy of known size (for counter scaling)")
+    ap.add_argument("--ingest", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="write profiles/counters_<workload>.json from rocprofv3 --pmc outputs")
+    ap.add_argument("--kernel-name", default="stream_kernel", help="kernel name part for --ingest")
     args = ap.parse_args()
+    if args.ingest:
+        return ingest_counters(args)
+    if args.copy_calibration:
+        return copy_calibration()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the projection path is single-GPU in this build "
@@ -180,7 +277,7 @@ def main() -> int:
     gbs = w.alg_bytes() / sec / 1e9
     tflops = w.alg_flops() / sec / 1e12
     hbm_bound = w.M <= 64
-    traffic = load_traffic(w.name, 1)
+    traffic = load_traffic(w.name)
     if hbm_bound:
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic}

@@ -23,8 +23,7 @@ struct Args {
     void *Y;               // fp32 / bf16 [M, N]
     int64_t M, N, K;
     int epi, out;
-    float *ws;             // split-K partials (library-owned)
-    unsigned *counters;    // split-K completion counters, zero between calls
+    float *ws;             // split-K partials [S][M][N] (library-owned)
     const uint16_t *zeros; // >= 64 zero bytes in device memory, for masked loads
 };
 
@@ -80,6 +79,10 @@ __device__ __forceinline__ void dma16(const void *src, void *lds_wave_base) {
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// s_waitcnt lgkmcnt(0) (vmcnt and expcnt left at their maxima), emitted as a
+// real waitcnt instruction so the compiler's own wait insertion sees it.
+__device__ __forceinline__ void lds_wait_all() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 __device__ __forceinline__ bf16x8 load16_nt(const uint16_t *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(p));

@@ -6,17 +6,6 @@
 
 namespace proj {
 
-// Weight-streaming split-K kernel for small M (skinny.hip).
-struct SkinnyVariant {
-    const char *family;
-    int mt, nt, waves, unroll;
-    bool nontemporal;
-    bool rotate;  // per-workgroup rotation of the K start
-    hipError_t (*launch)(const Args &, int splits, hipStream_t);
-};
-extern const SkinnyVariant kSkinnyVariants[];
-extern const int kNumSkinnyVariants;
-
 // Weight-streaming kernel staged through an LDS ring (stream.hip); with
 // splits > 1 a second kernel adds the partials and applies the epilogue.
 struct StreamVariant {
@@ -31,7 +20,7 @@ extern const int kNumStreamVariants;
 // LDS-pipelined MFMA GEMM for large M (gemm.hip).
 struct GemmVariant {
     const char *family;
-    int bm, bn, bk, waves_m, waves_n;
+    int bm, bn, bk, waves_m, waves_n, group_m;
     hipError_t (*launch)(const Args &, hipStream_t);
     hipError_t (*prepare)();  // one-time function attributes (LDS size)
 };

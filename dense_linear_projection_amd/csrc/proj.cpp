@@ -35,7 +35,6 @@ namespace {
 constexpr uint32_t kMagic = 0x50524f4au;   // live context
 constexpr uint32_t kDead = 0xdeadbeefu;    // destroyed context
 constexpr size_t kWorkspaceBytes = 64ull << 20;
-constexpr size_t kCounters = 1u << 20;
 constexpr size_t kZeroBytes = 256;
 constexpr size_t kFlushBytes = 512ull << 20;  // larger than the last-level cache
 
@@ -47,12 +46,12 @@ struct Key {
     }
 };
 
-enum Kind { KIND_SKINNY = 0, KIND_GEMM = 1, KIND_GENERIC = 2, KIND_STREAM = 3 };
+enum Kind { KIND_STREAM = 0, KIND_GEMM = 1, KIND_GENERIC = 2 };
 
 struct Candidate {
     Kind kind;
     int variant;  // index into the kernel table
-    int splits;   // skinny only
+    int splits;   // stream only: K ranges over workgroups
     std::string name;
 };
 
@@ -68,7 +67,6 @@ struct proj_ctx {
     uint32_t magic;
     int device;
     float *ws;
-    unsigned *counters;
     uint16_t *zeros;
     void *flush;
     std::map<Key, Plan> plans;
@@ -126,20 +124,6 @@ int mt_for(int64_t M) {
     return need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 0;
 }
 
-int64_t skinny_tiles(const SkinnyVariant &v, int64_t N) { return (N + 16 * v.nt - 1) / (16 * v.nt); }
-
-size_t skinny_ws_bytes(const SkinnyVariant &v, int64_t N, int S) {
-    if (S <= 1) return 0;
-    return static_cast<size_t>(skinny_tiles(v, N)) * S * v.mt * v.nt * 256 * sizeof(float);
-}
-
-std::string skinny_name(const SkinnyVariant &v, int S) {
-    char b[96];
-    snprintf(b, sizeof b, "skinny_mt%d_nt%d_w%d_u%d%s%s_s%d", v.mt, v.nt, v.waves, v.unroll,
-             v.nontemporal ? "_ntl" : "", v.rotate ? "_rot" : "", S);
-    return b;
-}
-
 std::string stream_name(const StreamVariant &v, int S) {
     char b[96];
     snprintf(b, sizeof b, "stream_mt%d_nt%d_w%d_k%d_d%d_s%d", v.mt, v.nt, v.waves, v.kc, v.depth, S);
@@ -148,7 +132,7 @@ std::string stream_name(const StreamVariant &v, int S) {
 
 std::string gemm_name(const GemmVariant &v) {
     char b[96];
-    snprintf(b, sizeof b, "gemm_%dx%dx%d_w%dx%d", v.bm, v.bn, v.bk, v.waves_m, v.waves_n);
+    snprintf(b, sizeof b, "%s_%dx%dx%d_w%dx%d_g%d", v.family, v.bm, v.bn, v.bk, v.waves_m, v.waves_n, v.group_m);
     return b;
 }
 
@@ -159,20 +143,6 @@ std::vector<Candidate> candidates(const Key &k) {
     std::vector<Candidate> out;
     if (k.aligned && k.K > 0) {
         const int mt = mt_for(k.M);
-        if (mt > 0) {
-            const int64_t T = (k.K + 31) / 32;
-            for (int i = 0; i < kNumSkinnyVariants; ++i) {
-                const SkinnyVariant &v = kSkinnyVariants[i];
-                if (v.mt != mt) continue;
-                const int64_t tiles = skinny_tiles(v, k.N);
-                for (int S : {1, 2, 3, 4, 6, 8, 16}) {
-                    if (S > 1 && (S > T || static_cast<size_t>(tiles) > kCounters)) continue;
-                    if (skinny_ws_bytes(v, k.N, S) > kWorkspaceBytes) continue;
-                    if (tiles * S > 0x7fffffff) continue;
-                    out.push_back({KIND_SKINNY, i, S, skinny_name(v, S)});
-                }
-            }
-        }
         if (mt > 0) {
             for (int i = 0; i < kNumStreamVariants; ++i) {
                 const StreamVariant &v = kStreamVariants[i];
@@ -206,15 +176,16 @@ Candidate default_candidate(const Key &k) {
         return nullptr;
     };
     if (mt_for(k.M) > 0) {
-        // smallest split count that gives at least one workgroup per CU
+        // 32 rows per workgroup, 256-byte row segments, 4 stages in flight,
+        // and the smallest split count that gives every CU a workgroup
         for (const Candidate &x : c) {
-            if (x.kind != KIND_SKINNY) continue;
-            const SkinnyVariant &v = kSkinnyVariants[x.variant];
-            if (v.nt != 1 || v.waves != 8 || v.unroll != 4 || v.nontemporal || v.rotate) continue;
-            if (skinny_tiles(v, k.N) * x.splits >= 256 || x.splits == 16) return x;
+            if (x.kind != KIND_STREAM) continue;
+            const StreamVariant &v = kStreamVariants[x.variant];
+            if (v.nt != 2 || v.kc != 128 || v.depth != 5 || v.waves != 4) continue;
+            if (((k.N + 31) / 32) * x.splits >= 256 || x.splits == 8) return x;
         }
     }
-    if (const Candidate *g = find("gemm_256x256x64_w2x2")) return *g;
+    if (const Candidate *g = find("gemm_256x256x64_w2x2_g4")) return *g;
     for (const Candidate &x : c)
         if (x.kind == KIND_GEMM) return x;
     return c.front();
@@ -233,14 +204,12 @@ Args make_args(proj_ctx *c, const void *X, const void *W, const void *bias, int 
     a.epi = epi;
     a.out = out;
     a.ws = c->ws;
-    a.counters = c->counters;
     a.zeros = c->zeros;
     return a;
 }
 
 hipError_t launch(const Candidate &cand, const Args &a, hipStream_t st) {
     switch (cand.kind) {
-        case KIND_SKINNY: return kSkinnyVariants[cand.variant].launch(a, cand.splits, st);
         case KIND_GEMM: return kGemmVariants[cand.variant].launch(a, st);
         case KIND_STREAM: return kStreamVariants[cand.variant].launch(a, cand.splits, st);
         default: return launch_generic(a, st);
@@ -416,20 +385,16 @@ proj_status proj_create(proj_ctx **out, int device) {
     c->magic = kMagic;
     c->device = device;
     c->ws = nullptr;
-    c->counters = nullptr;
     c->zeros = nullptr;
     c->flush = nullptr;
     bool ok = hipMalloc(&c->ws, kWorkspaceBytes) == hipSuccess &&
-              hipMalloc(&c->counters, kCounters * sizeof(unsigned)) == hipSuccess &&
               hipMalloc(&c->zeros, kZeroBytes) == hipSuccess &&
-              hipMemset(c->counters, 0, kCounters * sizeof(unsigned)) == hipSuccess &&
               hipMemset(c->zeros, 0, kZeroBytes) == hipSuccess;
     for (int i = 0; ok && i < kNumGemmVariants; ++i) ok = kGemmVariants[i].prepare() == hipSuccess;
     for (int i = 0; ok && i < kNumStreamVariants; ++i) ok = kStreamVariants[i].prepare() == hipSuccess;
     ok = ok && hipDeviceSynchronize() == hipSuccess;
     if (!ok) {
         hipFree(c->ws);
-        hipFree(c->counters);
         hipFree(c->zeros);
         delete c;
         return PROJ_ERR_HIP;
@@ -456,7 +421,6 @@ proj_status proj_destroy(proj_ctx *ctx) {
         DeviceGuard g(ctx->device);
         hipDeviceSynchronize();
         hipFree(ctx->ws);
-        hipFree(ctx->counters);
         hipFree(ctx->zeros);
         if (ctx->flush) hipFree(ctx->flush);
     }

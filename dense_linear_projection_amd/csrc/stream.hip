@@ -221,9 +221,12 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(Args a, int S) {
 
 // ---------------------------------------------------------------- registry
 #define PROJ_STREAM_VARIANTS(X)                                                                  \
-    X(1, 1, 8, 256, 4) X(1, 2, 8, 256, 4) X(1, 2, 8, 256, 3) X(1, 1, 8, 512, 3)                  \
-    X(1, 2, 4, 256, 4) X(1, 4, 8, 256, 3) X(1, 2, 8, 512, 3) X(2, 2, 8, 256, 4)                  \
-    X(4, 2, 8, 256, 3) X(4, 4, 8, 256, 2) X(4, 4, 4, 128, 4) X(4, 2, 4, 128, 4) X(4, 7, 4, 128, 3)
+    X(1, 1, 8, 256, 4) X(1, 2, 8, 256, 4) X(1, 2, 8, 256, 3) X(1, 4, 8, 256, 3)                  \
+    X(1, 1, 4, 128, 9) X(1, 1, 4, 128, 6) X(1, 2, 4, 128, 5) X(1, 2, 4, 128, 7)                  \
+    X(1, 2, 2, 128, 5) X(1, 4, 4, 128, 4) X(1, 4, 4, 128, 3)                                      \
+    X(2, 2, 8, 256, 4) X(2, 2, 4, 128, 5) X(2, 4, 4, 128, 4)                                      \
+    X(4, 2, 8, 256, 3) X(4, 4, 8, 256, 2) X(4, 4, 4, 128, 4) X(4, 4, 4, 128, 5)                  \
+    X(4, 2, 4, 128, 4) X(4, 2, 4, 128, 6) X(4, 7, 4, 128, 3)
 
 #define PROJ_STREAM_INST(MT, NT, WV, KC, D) \
     template __global__ void stream_kernel<MT, NT, WV, KC, D>(Args, int);

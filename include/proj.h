@@ -38,9 +38,9 @@
  * Arguments are validated before any HIP call.  HIP failures return
  * PROJ_ERR_HIP and the message is kept in the context (proj_last_error).
  *
- * Threading: a context holds one split-K workspace.  Calls that may run at
- * the same time on the GPU (different streams) must use different contexts,
- * or the caller must order them.  Host-side, a context may be used from one
+ * Threading: a context holds one split-K partial workspace.  Calls that may
+ * run at the same time on the GPU (different streams) must use different
+ * contexts, or the caller must order them.  Host-side, a context may be used from one
  * thread at a time.
  */
 #ifndef PROJ_H
@@ -78,8 +78,8 @@ typedef enum {
     PROJ_OUT_BF16 = 1  /* bf16 output, round to nearest even from fp32 */
 } proj_out_dtype;
 
-/* Create a context on HIP device `device`.  Allocates the split-K workspace
- * and completion counters (zeroed) and a zero page used for masked loads.
+/* Create a context on HIP device `device`.  Allocates the split-K partial
+ * workspace (64 MiB) and a zero page used for masked loads.
  * Returns PROJ_ERR_INVALID_ARG if ctx is NULL, PROJ_ERR_HIP if the device
  * cannot be used (e.g. no GPU), PROJ_ERR_UNSUPPORTED if it is not gfx950. */
 proj_status proj_create(proj_ctx **ctx, int device);
@@ -102,7 +102,8 @@ proj_status proj_create(proj_ctx **ctx, int device);
  * cached as "default" (a later uncaptured proj_tune replaces it).
  *
  * Capture: proj_run never allocates, synchronises or touches the host
- * during capture; split-K completion counters reset themselves, so a
+ * during capture, and keeps no state between calls on the device (split-K
+ * partials are fully rewritten by every call before they are summed), so a
  * captured graph can be replayed any number of times with fresh X.  */
 proj_status proj_run(proj_ctx *ctx, const void *X, const void *W, const void *bias,
                      int epilogue, int64_t M, int64_t N, int64_t K, void *Y,
@@ -126,7 +127,7 @@ const char *proj_status_string(int status);
 const char *proj_last_error(const proj_ctx *ctx);
 
 /* Introspection: the plan cached for a shape key, as text, e.g.
- * "skinny mt1 nt2 w8 u4 s1 (tuned 18.2us)".  PROJ_ERR_INVALID_ARG if no plan
+ * "stream_mt1_nt2_w4_k128_d5_s1 (tuned 24.20us)".  PROJ_ERR_INVALID_ARG if no plan
  * is cached for that key or buf is too small. */
 proj_status proj_get_plan(proj_ctx *ctx, int64_t M, int64_t N, int64_t K, int epilogue,
                           int out_dtype, int aligned16, char *buf, size_t buflen);

@@ -2,7 +2,7 @@
 finds at replay time (worklog "How I made Muse's GPU projections 1.32x
 faster in the Open Kernel Challenge", section "Fresh graph replay is a
 correctness test too": [2,3] -> [5,8,5], then [3,1] -> [11,5,-3]), and
-split-K counters reset themselves so every replay is right."""
+split-K partial sums are rebuilt by every replay."""
 import numpy as np
 import pytest
 

@@ -1,7 +1,7 @@
 """Identities the pages and the mathematics fix, checked on the GPU path for
 every kernel variant: worked examples, the transposed product, linearity,
 power-of-two scaling, one-hot probes, and fresh results on repeated calls
-(split-K counters and workspace must not leak between calls)."""
+(split-K partials must not leak between calls)."""
 import json
 import os
 
