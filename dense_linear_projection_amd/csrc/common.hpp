@@ -41,6 +41,21 @@ __device__ __forceinline__ float gelu_tanh(float v) {
     return v / (1.0f + __expf(-u2));
 }
 
+// The same GELU with a hardware reciprocal (about 1 ulp) in place of the
+// IEEE division: used on the large-M epilogues where the per-element cost
+// matters; the result differs from gelu_tanh by a few fp32 ulps.
+__device__ __forceinline__ float gelu_tanh_fast(float v) {
+    const float c2 = 2.0f * 0.7978845608028654f;
+    float u2 = c2 * (v + 0.044715f * v * v * v);
+    return v * __builtin_amdgcn_rcpf(1.0f + __expf(-u2));
+}
+
+__device__ __forceinline__ float apply_epilogue_fast(float acc, int epi, float bias) {
+    float v = acc + bias;  // bias is 0 when the epilogue has none
+    if (epi & 2) v = gelu_tanh_fast(v);
+    return v;
+}
+
 // bias (fp32-widened bf16) is added to the finished fp32 sum, then GELU.
 __device__ __forceinline__ float apply_epilogue(float acc, int epi, float bias) {
     float v = acc;
@@ -83,6 +98,20 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 // s_waitcnt lgkmcnt(0) (vmcnt and expcnt left at their maxima), emitted as a
 // real waitcnt instruction so the compiler's own wait insertion sees it.
 __device__ __forceinline__ void lds_wait_all() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// s_waitcnt lgkmcnt(N): all but the N most recent LDS operations are done.
+template <int N>
+__device__ __forceinline__ void lds_wait_keep() {
+    static_assert(N >= 0 && N <= 15, "lgkmcnt range");
+    __builtin_amdgcn_s_waitcnt(0xC07F | (N << 8));
+}
+
+// s_waitcnt vmcnt(N): all but the N most recent vector memory operations are done.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 __device__ __forceinline__ bf16x8 load16_nt(const uint16_t *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(p));

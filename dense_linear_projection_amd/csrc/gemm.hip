@@ -30,6 +30,8 @@
 // GEMM + GELU epilogue row).  Rows beyond M or N read a clamped valid row and
 // are not stored.  The planner only picks this kernel when K % BK == 0 and X,
 // W are 16-byte aligned.
+#include <utility>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -324,6 +326,254 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
 }
 
+// Four-wave GEMM on a 4-deep ring of BK = 32 stages.  Each wave owns a
+// 128 x (BN/2) sub-tile (8 x FN accumulators of 16x16) and is the only wave
+// on its SIMD, so it must hide its own latencies:
+//   * a stage (256 rows of X and BN rows of W, 32 k each) is one k-step: 8
+//     groups of FN matrix ops, one group per 16-row fragment of A;
+//   * the A fragment for group g is read two groups ahead, and in the second
+//     half of stage t the B fragments and first two A fragments of stage t+1
+//     are read, so a stage starts with its operands already in registers;
+//   * one barrier per stage, in its middle (before group 4): each wave first
+//     waits for its own DMA copies of stage t+1 (vmcnt), the barrier then
+//     makes stage t+1 visible to all waves and proves that stage t-1's slot
+//     is no longer read, so the copies of stage t+3 go into that slot right
+//     after it (two stages of lead for the DMA);
+//   * rows of 64 bytes hold 16-byte chunks at position chunk ^ ((row >> 2) & 3),
+//     so the 16 rows of one fragment read fall on distinct LDS banks; the DMA
+//     writes lane i to position i, so the XOR picks each lane's source.
+// Scheduling fences keep each group's reads ahead of its matrix ops (the
+// compiler would otherwise sink each read to just before its first use).
+// Epilogue: bias, GELU and rounding to bf16 in registers, then the whole
+// tile is staged through LDS (XOR-swizzled by row group) and written with
+// 16-byte row-contiguous stores; partial tiles, fp32 output or an unaligned
+// Y store element by element.
+// Per-group counts of the ring pipeline: in the second half of a stage
+// (groups MID..FM-1) the next stage's FN B fragments and the PERW DMA copies
+// are spread evenly; every group also reads one A fragment.
+template <int FM, int FN, int PERW, int MID>
+struct RingPlan {
+    static constexpr int H = FM - MID;
+    static constexpr int NB = (FN + H - 1) / H;      // next-stage B fragments per group
+    static constexpr int NC = (PERW + H - 1) / H;    // DMA copies per group
+    static constexpr int b_lo(int g) { return g < MID ? 0 : ((g - MID) * NB < FN ? (g - MID) * NB : FN); }
+    static constexpr int b_hi(int g) { return g < MID ? 0 : ((g - MID + 1) * NB < FN ? (g - MID + 1) * NB : FN); }
+    static constexpr int c_lo(int g) { return g < MID ? 0 : ((g - MID) * NC < PERW ? (g - MID) * NC : PERW); }
+    static constexpr int c_hi(int g) { return g < MID ? 0 : ((g - MID + 1) * NC < PERW ? (g - MID + 1) * NC : PERW); }
+    // LDS reads issued in group g
+    static constexpr int reads(int g) { return 1 + b_hi(g) - b_lo(g); }
+    // before group g's own reads: every read but the previous group's has
+    // landed (group 0 follows the previous stage's last group; MID follows a
+    // full wait)
+    static constexpr int keep(int g) { return g == MID ? 0 : reads(g == 0 ? FM - 1 : g - 1); }
+};
+
+// lgkmcnt wait for group g of the ring pipeline (g folds to a constant once
+// the group loop is unrolled)
+template <class P, int... Gs>
+__device__ __forceinline__ void ring_wait(int g, std::integer_sequence<int, Gs...>) {
+    ((g == Gs ? lds_wait_keep<P::keep(Gs)>() : void()), ...);
+}
+
+template <int BN, int GM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_ring_kernel(Args a) {
+    constexpr int BM = 256, BK = 32, D = 4, WN = 2, NW = 4;
+    constexpr int TM = 128, TN = BN / 2;
+    constexpr int FM = TM / 16, FN = TN / 16;
+    constexpr int ROWB = BK * 2;                     // 64 bytes per row per stage
+    constexpr int STAGE = (BM + BN) * ROWB;
+    constexpr int A_BLK = BM / 16, B_BLK = BN / 16;  // 1 KB DMA blocks (16 rows)
+    constexpr int PERW = (A_BLK + B_BLK) / NW;       // DMA copies per wave per stage
+    constexpr int MID = FM / 2;                      // group before which the barrier sits
+    static_assert((A_BLK + B_BLK) % NW == 0, "copies divide over the waves");
+    using P = RingPlan<FM, FN, PERW, MID>;
+    static_assert(P::reads(FM - 1) <= 15 && P::reads(MID) <= 15, "lgkmcnt range");
+    static_assert(D * STAGE <= 160 * 1024 && BM * BN * 2 <= D * STAGE, "LDS budget");
+
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int64_t M = a.M, N = a.N, K = a.K;
+
+    const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    const int64_t G = tiles_m * tiles_n;
+    int64_t L = blockIdx.x;
+    if (G % 8 == 0) L = (L % 8) * (G / 8) + L / 8;
+    const int64_t per_group = GM * tiles_n;
+    const int64_t group = L / per_group;
+    const int64_t first_m = group * GM;
+    const int64_t gsz = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
+    const int64_t tm = first_m + (L % per_group) % gsz;
+    const int64_t tn = (L % per_group) / gsz;
+    const int64_t m0 = tm * BM, n0 = tn * BN;
+
+    // DMA sources: block b (16 rows) of a stage; lane l fills row 16b + l/4,
+    // position l%4, which holds chunk (l%4) ^ (l/16).
+    const int drow = lane >> 2;
+    const int dchunk = (lane & 3) ^ (lane >> 4);
+    const uint16_t *src[PERW];
+    int dst[PERW];
+#pragma unroll
+    for (int j = 0; j < PERW; ++j) {
+        const int blk = wave + j * NW;
+        if (blk < A_BLK) {
+            int64_t row = m0 + blk * 16 + drow;
+            if (row >= M) row = M - 1;
+            src[j] = a.X + row * K + dchunk * 8;
+        } else {
+            int64_t row = n0 + (blk - A_BLK) * 16 + drow;
+            if (row >= N) row = N - 1;
+            src[j] = a.W + row * K + dchunk * 8;
+        }
+        dst[j] = blk * 1024;
+    }
+    const int64_t KT = K / BK;
+    auto copy = [&](int j, int64_t t) {
+        // stages past the end re-read the last one into an idle slot
+        const int64_t tt = t < KT ? t : KT - 1;
+        dma16(src[j] + tt * BK, lds + static_cast<int>(t % D) * STAGE + dst[j]);
+    };
+
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int fr = lane & 15, fg = lane >> 4;
+    auto frag = [&](const char *base, int row) -> bf16x8 {
+        return *reinterpret_cast<const bf16x8 *>(base + row * ROWB + ((fg ^ ((row >> 2) & 3)) << 4));
+    };
+    auto stage_a = [&](int64_t t) -> const char * { return lds + static_cast<int>(t % D) * STAGE; };
+
+    if (KT > 0) {
+        // stages 0..2 in flight; stage 0 (and 1) landed and visible
+#pragma unroll
+        for (int j = 0; j < PERW; ++j) copy(j, 0);
+#pragma unroll
+        for (int j = 0; j < PERW; ++j) copy(j, 1);
+#pragma unroll
+        for (int j = 0; j < PERW; ++j) copy(j, 2);
+        wait_vm<PERW>();
+        __syncthreads();
+    }
+
+    // Two fragment sets alternate between even and odd stages, so the next
+    // stage's fragments are prefetched into the idle set without copies.
+    bf16x8 b0[FN], b1[FN], a0[FM + 2], a1[FM + 2];
+    {
+        const char *sa = stage_a(0), *sb = sa + BM * ROWB;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) b0[j] = frag(sb, wn * TN + j * 16 + fr);
+        a0[0] = frag(sa, wm * TM + fr);
+        a0[1] = frag(sa, wm * TM + 16 + fr);
+        lds_wait_all();
+    }
+
+    auto stage = [&](int64_t kt, bf16x8(&bc)[FN], bf16x8(&bn)[FN], bf16x8(&ac)[FM + 2], bf16x8(&an)[FM + 2]) {
+        const char *sa = stage_a(kt), *sb = sa + BM * ROWB;
+        const char *na = stage_a(kt + 1), *nb = na + BM * ROWB;
+#pragma unroll
+        for (int g = 0; g < FM; ++g) {
+            if (g == MID) {
+                // stage kt+1 landed for this wave (stage kt+2 may still fly),
+                // then for all waves; stage kt-1's slot is free
+                wait_vm<PERW>();
+                lds_wait_all();
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // reads issued at least one group ago have landed (the previous
+            // group's own reads may still fly)
+            ring_wait<P>(g, std::make_integer_sequence<int, FM>{});
+            if (g + 2 < FM)
+                ac[g + 2] = frag(sa, wm * TM + (g + 2) * 16 + fr);
+            else
+                an[g + 2 - FM] = frag(na, wm * TM + (g + 2 - FM) * 16 + fr);
+#pragma unroll
+            for (int q = P::b_lo(g); q < P::b_hi(g); ++q) bn[q] = frag(nb, wn * TN + q * 16 + fr);
+#pragma unroll
+            for (int q = P::c_lo(g); q < P::c_hi(g); ++q) copy(q, kt + 3);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[g][j] = mfma16x16x32(ac[g], bc[j], acc[g][j]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // KT is even: the planner offers this kernel only for K % 64 == 0
+    for (int64_t kt = 0; kt < KT; kt += 2) {
+        stage(kt, b0, b1, a0, a1);
+        stage(kt + 1, b1, b0, a1, a0);
+    }
+    wait_vm<0>();
+    lds_wait_all();
+    __syncthreads();
+
+    // ---- epilogue
+    const bool full = (m0 + BM <= M) && (n0 + BN <= N) && (N % 8 == 0) && a.out == OUT_BF16 &&
+                      (reinterpret_cast<uintptr_t>(a.Y) % 16 == 0);
+    float bias[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const int64_t n = n0 + wn * TN + j * 16 + fr;
+        bias[j] = ((a.epi & 1) && n < N) ? bf16_bits_to_f32(a.bias[n]) : 0.f;
+    }
+    if (full) {
+        // The tile goes to LDS as bf16 [BM][BN] with 16-column chunks XOR'd by
+        // the row's group of four ((row >> 2) & 3, which is this lane's fg for
+        // every value it holds), so one write's four row groups hit different
+        // banks; every address is then a per-lane base plus a constant.
+        uint16_t *t16 = reinterpret_cast<uint16_t *>(lds);
+        uint16_t *lbase = t16 + (wm * TM + fg * 4) * BN + fr;
+        const int epi = a.epi;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            uint16_t *cb = lbase + ((wn * TN + j * 16) ^ (fg << 4));
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    cb[(i * 16 + r) * BN] = f32_to_bf16_bits(apply_epilogue_fast(acc[i][j][r], epi, bias[j]));
+        }
+        __syncthreads();
+        constexpr int CPR = BN / 8;  // 16-byte chunks per row
+        if constexpr (256 % CPR == 0) {
+            constexpr int RPP = 256 / CPR;  // rows per pass of the workgroup
+            const int prow = tid / CPR, ch = tid % CPR;
+            const uint16_t *lsrc = t16 + prow * BN;
+            uint16_t *gdst = static_cast<uint16_t *>(a.Y) + (m0 + prow) * N + n0 + ch * 8;
+#pragma unroll 8
+            for (int p = 0; p < BM / RPP; ++p) {
+                const int row = prow + p * RPP;
+                const int pcol = (ch * 8) ^ (((row >> 2) & 3) << 4);
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(lsrc + p * RPP * BN + pcol);
+                *reinterpret_cast<u32x4 *>(gdst + static_cast<int64_t>(p) * RPP * N) = v;
+            }
+        } else {
+#pragma unroll 4
+            for (int c = tid; c < BM * CPR; c += 256) {
+                const int row = c / CPR, ch = c % CPR;
+                const u32x4 v =
+                    *reinterpret_cast<const u32x4 *>(t16 + row * BN + ((ch * 8) ^ (((row >> 2) & 3) << 4)));
+                *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.Y) + (m0 + row) * N + n0 + ch * 8) = v;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int64_t n = n0 + wn * TN + j * 16 + fr;
+            if (n >= N) continue;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t m = m0 + wm * TM + i * 16 + fg * 4 + r;
+                    if (m < M) store_out(a.Y, a.out, m * N + n, apply_epilogue(acc[i][j][r], a.epi, bias[j]));
+                }
+        }
+    }
+}
+
 // One list drives both compilation passes (device: kernel instantiation,
 // host: launch table).
 #define PROJ_GEMM_VARIANTS(X)                                                                    \
@@ -337,6 +587,10 @@ PROJ_GEMM_VARIANTS(PROJ_GEMM_INST)
 #define PROJ_GEMM_PIPE_VARIANTS(X) X(256, 4, false, 1) X(256, 4, true, 1) X(256, 4, true, 2) X(256, 4, false, 2)
 #define PROJ_GEMM_PIPE_INST(BN, GM, E, PD) template __global__ void gemm_pipe_kernel<BN, GM, E, PD>(Args);
 PROJ_GEMM_PIPE_VARIANTS(PROJ_GEMM_PIPE_INST)
+
+#define PROJ_GEMM_RING_VARIANTS(X) X(256, 4) X(256, 8) X(192, 4) X(128, 4)
+#define PROJ_GEMM_RING_INST(BN, GM) template __global__ void gemm_ring_kernel<BN, GM>(Args);
+PROJ_GEMM_RING_VARIANTS(PROJ_GEMM_RING_INST)
 
 #ifndef __HIP_DEVICE_COMPILE__
 template <int BM, int BN, int BK, int WM, int WN, int GM>
@@ -375,12 +629,31 @@ static hipError_t launch_gemm_pipe(const Args &a, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <int BN, int GM>
+static hipError_t prepare_gemm_ring() {
+    auto fn = gemm_ring_kernel<BN, GM>;
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               4 * (256 + BN) * 64);
+}
+
+template <int BN, int GM>
+static hipError_t launch_gemm_ring(const Args &a, hipStream_t st) {
+    const int64_t G = ((a.M + 255) / 256) * ((a.N + BN - 1) / BN);
+    if (G <= 0 || G > 0x7fffffff) return hipErrorInvalidConfiguration;
+    constexpr int lds_bytes = 4 * (256 + BN) * 64;
+    hipLaunchKernelGGL((gemm_ring_kernel<BN, GM>), dim3(static_cast<unsigned>(G)), dim3(256), lds_bytes, st, a);
+    return hipGetLastError();
+}
+
 #define PROJ_GEMM_ENTRY(BM, BN, WM, WN, GM) \
-    {"gemm", BM, BN, 64, WM, WN, GM, &launch_gemm<BM, BN, 64, WM, WN, GM>, &prepare_gemm<BM, BN, 64, WM, WN, GM>},
+    {"gemm", BM, BN, 64, 64, WM, WN, GM, &launch_gemm<BM, BN, 64, WM, WN, GM>, &prepare_gemm<BM, BN, 64, WM, WN, GM>},
 #define PROJ_GEMM_PIPE_ENTRY(BN, GM, E, PD)                                                                    \
-    {E ? (PD == 2 ? "gemmpipe_e_p2" : "gemmpipe_e") : (PD == 2 ? "gemmpipe_p2" : "gemmpipe"), 256, BN, 64, 2, 2, GM, \
+    {E ? (PD == 2 ? "gemmpipe_e_p2" : "gemmpipe_e") : (PD == 2 ? "gemmpipe_p2" : "gemmpipe"), 256, BN, 64, 64, 2, 2, GM, \
      &launch_gemm_pipe<BN, GM, E, PD>, &prepare_gemm_pipe<BN, GM, E, PD>},
-const GemmVariant kGemmVariants[] = {PROJ_GEMM_VARIANTS(PROJ_GEMM_ENTRY) PROJ_GEMM_PIPE_VARIANTS(PROJ_GEMM_PIPE_ENTRY)};
+#define PROJ_GEMM_RING_ENTRY(BN, GM) \
+    {"gemmring", 256, BN, 32, 64, 2, 2, GM, &launch_gemm_ring<BN, GM>, &prepare_gemm_ring<BN, GM>},
+const GemmVariant kGemmVariants[] = {PROJ_GEMM_VARIANTS(PROJ_GEMM_ENTRY) PROJ_GEMM_PIPE_VARIANTS(PROJ_GEMM_PIPE_ENTRY)
+                                         PROJ_GEMM_RING_VARIANTS(PROJ_GEMM_RING_ENTRY)};
 const int kNumGemmVariants = sizeof(kGemmVariants) / sizeof(kGemmVariants[0]);
 #endif
 

@@ -20,7 +20,7 @@ extern const int kNumStreamVariants;
 // LDS-pipelined MFMA GEMM for large M (gemm.hip).
 struct GemmVariant {
     const char *family;
-    int bm, bn, bk, waves_m, waves_n, group_m;
+    int bm, bn, bk, kmult, waves_m, waves_n, group_m;  // kmult: K must be a multiple of it
     hipError_t (*launch)(const Args &, hipStream_t);
     hipError_t (*prepare)();  // one-time function attributes (LDS size)
 };

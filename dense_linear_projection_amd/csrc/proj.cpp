@@ -159,7 +159,7 @@ std::vector<Candidate> candidates(const Key &k) {
         }
         for (int i = 0; i < kNumGemmVariants; ++i) {
             const GemmVariant &v = kGemmVariants[i];
-            if (k.K % v.bk != 0) continue;
+            if (k.K % v.kmult != 0) continue;
             out.push_back({KIND_GEMM, i, 1, gemm_name(v)});
         }
     }

@@ -41,11 +41,6 @@
 
 namespace proj {
 
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
 // wait until at most `ahead` stages of PERW copies are still in flight
 template <int PERW, int MAXAHEAD>
 __device__ __forceinline__ void wait_stages(int ahead) {
