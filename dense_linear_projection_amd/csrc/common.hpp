@@ -82,6 +82,13 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// 32x32x16 bf16 matrix op.  Lane l supplies row (A) / column (B) l % 32 and
+// k elements 8 (l / 32) .. +7; element v of the result is row
+// 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32.
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ bf16x8 load16(const uint16_t *p) {
     return *reinterpret_cast<const bf16x8 *>(p);
 }
@@ -91,6 +98,21 @@ __device__ __forceinline__ bf16x8 load16(const uint16_t *p) {
 // lds_wave_base must be the same for the whole wave.
 __device__ __forceinline__ void dma16(const void *src, void *lds_wave_base) {
     __builtin_amdgcn_global_load_lds(src, lds_wave_base, 16, 0, 0);
+}
+
+// Raw buffer resource over [base, base + bytes): loads at offsets at or past
+// `bytes` return zero instead of touching memory.  Word 3 is the gfx9 raw
+// (untyped, unswizzled) buffer format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+
+// 16-byte buffer -> LDS copy (buffer_load_dwordx4 ... lds): lane i reads
+// rsrc + voff + soff and writes lds_wave_base + 16*i.  soff and lds_wave_base
+// are wave-uniform, so a loop that only moves soff needs no vector arithmetic.
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void *lds_wave_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_wave_base, 16,
+                                             voff, soff, 0, 0);
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

@@ -30,6 +30,7 @@
 // GEMM + GELU epilogue row).  Rows beyond M or N read a clamped valid row and
 // are not stored.  The planner only picks this kernel when K % BK == 0 and X,
 // W are 16-byte aligned.
+#include <atomic>
 #include <utility>
 
 #include "common.hpp"
@@ -339,9 +340,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 //     makes stage t+1 visible to all waves and proves that stage t-1's slot
 //     is no longer read, so the copies of stage t+3 go into that slot right
 //     after it (two stages of lead for the DMA);
-//   * rows of 64 bytes hold 16-byte chunks at position chunk ^ ((row >> 2) & 3),
-//     so the 16 rows of one fragment read fall on distinct LDS banks; the DMA
-//     writes lane i to position i, so the XOR picks each lane's source.
+//   * rows of 64 bytes hold 16-byte chunks at position chunk ^ ((row >> 1) & 3):
+//     a 16-byte LDS read is served eight lanes at a time over 128 bytes of
+//     banks, and eight consecutive rows then cover all eight 16-byte bank
+//     groups; the DMA writes lane i to position i, so the XOR picks each
+//     lane's source.
 // Scheduling fences keep each group's reads ahead of its matrix ops (the
 // compiler would otherwise sink each read to just before its first use).
 // Epilogue: bias, GELU and rounding to bf16 in registers, then the whole
@@ -391,7 +394,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     static_assert(D * STAGE <= 160 * 1024 && BM * BN * 2 <= D * STAGE, "LDS budget");
 
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar
     const int wm = wave / WN, wn = wave % WN;
     const int64_t M = a.M, N = a.N, K = a.K;
 
@@ -407,31 +411,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int64_t tn = (L % per_group) / gsz;
     const int64_t m0 = tm * BM, n0 = tn * BN;
 
-    // DMA sources: block b (16 rows) of a stage; lane l fills row 16b + l/4,
-    // position l%4, which holds chunk (l%4) ^ (l/16).
+    // DMA: block b (16 rows) of a stage is one 1 KB copy; lane l fills row
+    // 16b + l/4, position l%4, which holds chunk (l%4) ^ ((l/8)%4).  The
+    // first A_BLK/NW copies of each wave are X blocks, the rest W blocks.
+    // Each operand is read through a buffer resource over the tile's valid
+    // rows: rows past M or N read as zero, the per-lane offset is fixed for
+    // the whole loop and the k offset is a scalar.
     const int drow = lane >> 2;
-    const int dchunk = (lane & 3) ^ (lane >> 4);
-    const uint16_t *src[PERW];
-    int dst[PERW];
+    const int dchunk = (lane & 3) ^ ((lane >> 3) & 3);
+    const int64_t rows_a = (M - m0) < BM ? (M - m0) : BM;
+    const int64_t rows_b = (N - n0) < BN ? (N - n0) : BN;
+    const __amdgpu_buffer_rsrc_t rsrc_a = buffer_rsrc(a.X + m0 * K, static_cast<uint32_t>(rows_a * K * 2));
+    const __amdgpu_buffer_rsrc_t rsrc_b = buffer_rsrc(a.W + n0 * K, static_cast<uint32_t>(rows_b * K * 2));
+    constexpr int PA = A_BLK / NW;
+    uint32_t voff[PERW];
 #pragma unroll
     for (int j = 0; j < PERW; ++j) {
-        const int blk = wave + j * NW;
-        if (blk < A_BLK) {
-            int64_t row = m0 + blk * 16 + drow;
-            if (row >= M) row = M - 1;
-            src[j] = a.X + row * K + dchunk * 8;
-        } else {
-            int64_t row = n0 + (blk - A_BLK) * 16 + drow;
-            if (row >= N) row = N - 1;
-            src[j] = a.W + row * K + dchunk * 8;
-        }
-        dst[j] = blk * 1024;
+        const int r = (j < PA ? (wave + j * NW) : (wave + (j - PA) * NW)) * 16 + drow;
+        voff[j] = static_cast<uint32_t>(r * K * 2 + dchunk * 16);
     }
     const int64_t KT = K / BK;
     auto copy = [&](int j, int64_t t) {
         // stages past the end re-read the last one into an idle slot
-        const int64_t tt = t < KT ? t : KT - 1;
-        dma16(src[j] + tt * BK, lds + static_cast<int>(t % D) * STAGE + dst[j]);
+        const uint32_t soff = static_cast<uint32_t>((t < KT ? t : KT - 1) * (BK * 2));
+        const int blk = j < PA ? wave + j * NW : A_BLK + wave + (j - PA) * NW;
+        char *dst = lds + static_cast<int>(t % D) * STAGE + blk * 1024;
+        dma16_buf(j < PA ? rsrc_a : rsrc_b, voff[j], soff, dst);
     };
 
     f32x4 acc[FM][FN];
@@ -442,7 +447,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     const int fr = lane & 15, fg = lane >> 4;
     auto frag = [&](const char *base, int row) -> bf16x8 {
-        return *reinterpret_cast<const bf16x8 *>(base + row * ROWB + ((fg ^ ((row >> 2) & 3)) << 4));
+        return *reinterpret_cast<const bf16x8 *>(base + row * ROWB + ((fg ^ ((row >> 1) & 3)) << 4));
     };
     auto stage_a = [&](int64_t t) -> const char * { return lds + static_cast<int>(t % D) * STAGE; };
 
@@ -574,6 +579,262 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
 }
 
+// The same four-wave ring with 32x32x16 matrix ops: a wave's 128 x (BN/2)
+// sub-tile is 4 x FN blocks of 32x32 (16 accumulators of 16 floats for
+// BN = 256), and a BK = 32 stage is two k-halves.  Half the matrix-op
+// instructions of the 16x16 form for the same work, and every group reads
+// exactly one A and at most ceil(FN/4) B fragments:
+//   * group g = 4h + i runs the FN matrix ops of A block i, k-half h;
+//   * the A fragment of group g is read two groups ahead (the last two
+//     groups read the next stage's first two);
+//   * k-half 1 B fragments of the current stage are read in groups 0..3,
+//     k-half 0 B fragments of the next stage in groups 4..7, so a stage
+//     starts with its first operands in registers;
+//   * barrier, DMA ring, LDS layout and swizzle as in the 16x16 ring.
+// Epilogue: the tile is staged through LDS as bf16, 64-column halves XOR'd
+// by bit 2 of the row so that the two half-waves' rows (4 apart) write
+// different banks, then written with 16-byte row-contiguous stores.
+template <int BN, int GM, int D, bool PERSIST>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_ring32_kernel(Args a) {
+    constexpr int BM = 256, BK = 32, WN = 2, NW = 4;
+    static_assert(D == 4 || D == 5, "ring depth");
+    constexpr int TM = 128, TN = BN / 2;
+    constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr int NG = 2 * FM;                       // groups per stage
+    constexpr int MID = NG / 2;                      // group before which the barrier sits
+    constexpr int ROWB = BK * 2;                     // 64 bytes per row per stage
+    constexpr int STAGE = (BM + BN) * ROWB;
+    constexpr int A_BLK = BM / 16, B_BLK = BN / 16;  // 1 KB DMA blocks (16 rows)
+    constexpr int PERW = (A_BLK + B_BLK) / NW;       // DMA copies per wave per stage
+    constexpr int PA = A_BLK / NW;
+    constexpr int NBG = (FN + MID - 1) / MID;        // B fragments read per group
+    // DMA schedule.  D = 4: the copies of stage t+3 are issued in the second
+    // half of stage t (after the barrier frees the slot of stage t-1).
+    // D = 5: one copy per group -- the first PH copies of stage t+4 in the
+    // second half of stage t, the rest of stage t+3 in the first half of
+    // stage t; a slot is then refilled three stages before it is read.
+    constexpr int PH = D == 4 ? PERW : (PERW + 1) / 2;
+    constexpr int NC1 = (PH + MID - 1) / MID;               // per group, second half
+    constexpr int NC2 = (PERW - PH + MID - 1) / MID;        // per group, first half (D = 5)
+    constexpr int LEAD = D == 4 ? PERW : 2 * PERW;          // copies still in flight at the barrier
+    static_assert(A_BLK % NW == 0 && B_BLK % NW == 0, "copies divide over the waves");
+    static_assert(1 + NBG <= 15, "lgkmcnt range");
+    static_assert(D * STAGE <= 160 * 1024 && BM * BN * 2 <= D * STAGE, "LDS budget");
+    static_assert(LEAD + PH <= 63, "vmcnt range");
+    static_assert(BN % 64 == 0, "epilogue swizzle works on 64-column halves");
+
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const int64_t M = a.M, N = a.N, K = a.K;
+
+    const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    const int64_t G = tiles_m * tiles_n;
+    // Persistent form: the grid is at most one workgroup per CU and each
+    // workgroup walks tiles blockIdx.x, + gridDim.x, ...  With a grid that is
+    // a multiple of 8 those tiles stay on the workgroup's XCD, whose tile
+    // range the renumbering below makes contiguous.
+    for (int64_t tile = blockIdx.x; tile < G; tile += (PERSIST ? gridDim.x : G)) {
+    int64_t L = tile;
+    if (G % 8 == 0) L = (L % 8) * (G / 8) + L / 8;
+    const int64_t per_group = GM * tiles_n;
+    const int64_t group = L / per_group;
+    const int64_t first_m = group * GM;
+    const int64_t gsz = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
+    const int64_t tm = first_m + (L % per_group) % gsz;
+    const int64_t tn = (L % per_group) / gsz;
+    const int64_t m0 = tm * BM, n0 = tn * BN;
+
+    // DMA (as in the 16x16 ring): lane l fills row 16b + l/4, position l%4,
+    // which holds chunk (l%4) ^ ((l/8)%4); rows past M or N read as zero.
+    const int drow = lane >> 2;
+    const int dchunk = (lane & 3) ^ ((lane >> 3) & 3);
+    const int64_t rows_a = (M - m0) < BM ? (M - m0) : BM;
+    const int64_t rows_b = (N - n0) < BN ? (N - n0) : BN;
+    const __amdgpu_buffer_rsrc_t rsrc_a = buffer_rsrc(a.X + m0 * K, static_cast<uint32_t>(rows_a * K * 2));
+    const __amdgpu_buffer_rsrc_t rsrc_b = buffer_rsrc(a.W + n0 * K, static_cast<uint32_t>(rows_b * K * 2));
+    uint32_t voff[PERW];
+#pragma unroll
+    for (int j = 0; j < PERW; ++j) {
+        const int r = (j < PA ? (wave + j * NW) : (wave + (j - PA) * NW)) * 16 + drow;
+        voff[j] = static_cast<uint32_t>(r * K * 2 + dchunk * 16);
+    }
+    const int KT = static_cast<int>(K / BK);  // K < 2^22 (planner limit)
+    // stages past the end go through an empty resource: no memory traffic,
+    // but the copy still counts for the vmcnt waits
+    const __amdgpu_buffer_rsrc_t rsrc_none = buffer_rsrc(a.X, 0);
+    // copy j of stage t into ring slot `slot` (= t % D, kept by the caller)
+    auto copy = [&](int j, int t, int slot) {
+        const uint32_t soff = static_cast<uint32_t>((t < KT ? t : KT - 1) * (BK * 2));
+        const int blk = j < PA ? wave + j * NW : A_BLK + wave + (j - PA) * NW;
+        dma16_buf(t < KT ? (j < PA ? rsrc_a : rsrc_b) : rsrc_none, voff[j], soff, lds + slot * STAGE + blk * 1024);
+    };
+    // slot of stage t + d given the slot of stage t
+    auto slot_add = [](int slot, int d) { return slot + d >= D ? slot + d - D : slot + d; };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    // fragment of 32 rows starting at row0 (a multiple of 32), k-half h:
+    // lane l reads row row0 + l%32, chunk 2h + l/32
+    const int fr = lane & 31, fq = lane >> 5;
+    const int sw = (fr >> 1) & 3;
+    auto frag = [&](const char *base, int row0, int h) -> bf16x8 {
+        return *reinterpret_cast<const bf16x8 *>(base + (row0 + fr) * ROWB + (((2 * h + fq) ^ sw) << 4));
+    };
+
+
+    if (KT > 0) {
+        // stages 0..2 (and the first part of stage 3 for D = 5) in flight;
+        // stage 0 landed and visible
+#pragma unroll
+        for (int j = 0; j < PERW; ++j) copy(j, 0, 0);
+#pragma unroll
+        for (int j = 0; j < PERW; ++j) copy(j, 1, 1);
+#pragma unroll
+        for (int j = 0; j < PERW; ++j) copy(j, 2, 2);
+        if constexpr (D == 5) {
+#pragma unroll
+            for (int j = 0; j < PH; ++j) copy(j, 3, 3);
+            wait_vm<2 * PERW + PH>();
+        } else {
+            wait_vm<2 * PERW>();
+        }
+        __syncthreads();
+    }
+
+    // b0x: k-half 0 fragments of the current stage (x alternates between
+    // stages), b1: k-half 1 of the current stage, a0x: A fragments by group
+    // (entries NG, NG+1 are the next stage's groups 0 and 1)
+    bf16x8 b0e[FN], b0o[FN], b1[FN], a0e[NG + 2], a0o[NG + 2];
+    {
+        const char *sa = lds, *sb = sa + BM * ROWB;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) b0e[j] = frag(sb, wn * TN + j * 32, 0);
+        a0e[0] = frag(sa, wm * TM, 0);
+        a0e[1] = frag(sa, wm * TM + 32, 0);
+        lds_wait_all();
+    }
+
+    auto stage = [&](int kt, int slot, bf16x8(&bc)[FN], bf16x8(&bn)[FN], bf16x8(&ac)[NG + 2],
+                     bf16x8(&an)[NG + 2]) {
+        const char *sa = lds + slot * STAGE, *sb = sa + BM * ROWB;
+        const char *na = lds + slot_add(slot, 1) * STAGE, *nb = na + BM * ROWB;
+        const int slot3 = slot_add(slot, 3), slot_last = slot_add(slot, D - 1);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const int h = g / FM, i = g % FM;
+            if (g == MID) {
+                // stage kt+1 landed for this wave, then for all waves; the
+                // slot of stage kt-1 is no longer read
+                wait_vm<LEAD>();
+                lds_wait_all();
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // every LDS read but the previous group's has landed
+            if (g == MID)
+                lds_wait_keep<0>();
+            else
+                lds_wait_keep<1 + NBG>();
+            const int gn = g + 2;
+            if (gn < NG)
+                ac[gn] = frag(sa, wm * TM + (gn % FM) * 32, gn / FM);
+            else
+                an[gn - NG] = frag(na, wm * TM + (gn - NG) * 32, 0);
+            const int q0 = (g % MID) * NBG;
+#pragma unroll
+            for (int q = q0; q < q0 + NBG && q < FN; ++q) {
+                if (g < MID)
+                    b1[q] = frag(sb, wn * TN + q * 32, 1);
+                else
+                    bn[q] = frag(nb, wn * TN + q * 32, 0);
+            }
+            if (g >= MID) {
+                const int c0 = (g - MID) * NC1;
+#pragma unroll
+                for (int c = c0; c < c0 + NC1 && c < PH; ++c) copy(c, kt + D - 1, slot_last);
+            } else if (D == 5) {
+                const int c0 = PH + g * NC2;
+#pragma unroll
+                for (int c = c0; c < c0 + NC2 && c < PERW; ++c) copy(c, kt + 3, slot3);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16(ac[g], h == 0 ? bc[j] : b1[j], acc[i][j]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // KT is even: the planner offers this kernel only for K % 64 == 0
+    for (int kt = 0, slot = 0; kt < KT; kt += 2) {
+        stage(kt, slot, b0e, b0o, a0e, a0o);
+        slot = slot_add(slot, 1);
+        stage(kt + 1, slot, b0o, b0e, a0o, a0e);
+        slot = slot_add(slot, 1);
+    }
+    wait_vm<0>();
+    lds_wait_all();
+    __syncthreads();
+
+    // ---- epilogue
+    const bool full = (m0 + BM <= M) && (n0 + BN <= N) && (N % 8 == 0) && a.out == OUT_BF16 &&
+                      (reinterpret_cast<uintptr_t>(a.Y) % 16 == 0);
+    float bias[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const int64_t n = n0 + wn * TN + j * 32 + fr;
+        bias[j] = ((a.epi & 1) && n < N) ? bf16_bits_to_f32(a.bias[n]) : 0.f;
+    }
+    if (full) {
+        // bf16 tile [BM][BN] in LDS; a value of row r, column c sits at column
+        // c ^ (32 * ((r >> 2) & 1)).  Row bit 2 is this lane's fq for every
+        // value it holds, so the XOR is one per-lane constant.
+        uint16_t *t16 = reinterpret_cast<uint16_t *>(lds);
+        uint16_t *lbase = t16 + (wm * TM + 4 * fq) * BN;
+        const int epi = a.epi;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            // the XOR applies to the whole column (j * 32 toggles bit 5)
+            uint16_t *cb = lbase + ((wn * TN + j * 32 + fr) ^ (fq << 5));
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    cb[(i * 32 + 8 * (v / 4) + (v % 4)) * BN] =
+                        f32_to_bf16_bits(apply_epilogue_fast(acc[i][j][v], epi, bias[j]));
+        }
+        __syncthreads();
+        constexpr int CPR = BN / 8;  // 16-byte chunks per row
+        for (int c = tid; c < BM * CPR; c += 256) {
+            const int row = c / CPR, ch = c % CPR;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(t16 + row * BN + ((ch * 8) ^ (((row >> 2) & 1) << 5)));
+            *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.Y) + (m0 + row) * N + n0 + ch * 8) = v;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int64_t n = n0 + wn * TN + j * 32 + fr;
+            if (n >= N) continue;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int64_t m = m0 + wm * TM + i * 32 + 8 * (v / 4) + 4 * fq + (v % 4);
+                    if (m < M) store_out(a.Y, a.out, m * N + n, apply_epilogue(acc[i][j][v], a.epi, bias[j]));
+                }
+        }
+    }
+    // the next tile's copies overwrite LDS that other waves may still read
+    if (PERSIST) __syncthreads();
+    }
+}
+
 // One list drives both compilation passes (device: kernel instantiation,
 // host: launch table).
 #define PROJ_GEMM_VARIANTS(X)                                                                    \
@@ -591,6 +852,11 @@ PROJ_GEMM_PIPE_VARIANTS(PROJ_GEMM_PIPE_INST)
 #define PROJ_GEMM_RING_VARIANTS(X) X(256, 4) X(256, 8) X(192, 4) X(128, 4)
 #define PROJ_GEMM_RING_INST(BN, GM) template __global__ void gemm_ring_kernel<BN, GM>(Args);
 PROJ_GEMM_RING_VARIANTS(PROJ_GEMM_RING_INST)
+
+#define PROJ_GEMM_RING32_VARIANTS(X) \
+    X(256, 4, 4, false) X(256, 4, 5, false) X(192, 4, 5, false) X(256, 4, 5, true) X(192, 4, 5, true) X(128, 4, 5, true)
+#define PROJ_GEMM_RING32_INST(BN, GM, D, P) template __global__ void gemm_ring32_kernel<BN, GM, D, P>(Args);
+PROJ_GEMM_RING32_VARIANTS(PROJ_GEMM_RING32_INST)
 
 #ifndef __HIP_DEVICE_COMPILE__
 template <int BM, int BN, int BK, int WM, int WN, int GM>
@@ -629,6 +895,9 @@ static hipError_t launch_gemm_pipe(const Args &a, hipStream_t st) {
     return hipGetLastError();
 }
 
+// The ring kernel addresses a 256-row tile through 32-bit buffer offsets.
+constexpr int64_t kRingMaxK = (int64_t{1} << 31) / (256 * 2);
+
 template <int BN, int GM>
 static hipError_t prepare_gemm_ring() {
     auto fn = gemm_ring_kernel<BN, GM>;
@@ -645,15 +914,53 @@ static hipError_t launch_gemm_ring(const Args &a, hipStream_t st) {
     return hipGetLastError();
 }
 
+// Number of CUs of the current device (all devices a process drives here are
+// the same part), read once.
+static int device_cus() {
+    static std::atomic<int> cus{0};
+    int n = cus.load(std::memory_order_relaxed);
+    if (n == 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cus.store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+template <int BN, int GM, int D, bool P>
+static hipError_t prepare_gemm_ring32() {
+    device_cus();
+    auto fn = gemm_ring32_kernel<BN, GM, D, P>;
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               D * (256 + BN) * 64);
+}
+
+template <int BN, int GM, int D, bool P>
+static hipError_t launch_gemm_ring32(const Args &a, hipStream_t st) {
+    const int64_t G = ((a.M + 255) / 256) * ((a.N + BN - 1) / BN);
+    if (G <= 0 || G > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const int64_t grid = P ? (G < device_cus() ? G : device_cus()) : G;
+    constexpr int lds_bytes = D * (256 + BN) * 64;
+    hipLaunchKernelGGL((gemm_ring32_kernel<BN, GM, D, P>), dim3(static_cast<unsigned>(grid)), dim3(256), lds_bytes, st,
+                       a);
+    return hipGetLastError();
+}
+
 #define PROJ_GEMM_ENTRY(BM, BN, WM, WN, GM) \
-    {"gemm", BM, BN, 64, 64, WM, WN, GM, &launch_gemm<BM, BN, 64, WM, WN, GM>, &prepare_gemm<BM, BN, 64, WM, WN, GM>},
+    {"gemm", BM, BN, 64, 64, WM, WN, GM, 0, &launch_gemm<BM, BN, 64, WM, WN, GM>, &prepare_gemm<BM, BN, 64, WM, WN, GM>},
 #define PROJ_GEMM_PIPE_ENTRY(BN, GM, E, PD)                                                                    \
-    {E ? (PD == 2 ? "gemmpipe_e_p2" : "gemmpipe_e") : (PD == 2 ? "gemmpipe_p2" : "gemmpipe"), 256, BN, 64, 64, 2, 2, GM, \
+    {E ? (PD == 2 ? "gemmpipe_e_p2" : "gemmpipe_e") : (PD == 2 ? "gemmpipe_p2" : "gemmpipe"), 256, BN, 64, 64, 2, 2, GM, 0, \
      &launch_gemm_pipe<BN, GM, E, PD>, &prepare_gemm_pipe<BN, GM, E, PD>},
 #define PROJ_GEMM_RING_ENTRY(BN, GM) \
-    {"gemmring", 256, BN, 32, 64, 2, 2, GM, &launch_gemm_ring<BN, GM>, &prepare_gemm_ring<BN, GM>},
+    {"gemmring", 256, BN, 32, 64, 2, 2, GM, kRingMaxK, &launch_gemm_ring<BN, GM>, &prepare_gemm_ring<BN, GM>},
+#define PROJ_GEMM_RING32_ENTRY(BN, GM, D, P)                                                         \
+    {P ? "gemmring32p" : (D == 5 ? "gemmring32d5" : "gemmring32"), 256, BN, 32, 64, 2, 2, GM, kRingMaxK, \
+     &launch_gemm_ring32<BN, GM, D, P>, &prepare_gemm_ring32<BN, GM, D, P>},
 const GemmVariant kGemmVariants[] = {PROJ_GEMM_VARIANTS(PROJ_GEMM_ENTRY) PROJ_GEMM_PIPE_VARIANTS(PROJ_GEMM_PIPE_ENTRY)
-                                         PROJ_GEMM_RING_VARIANTS(PROJ_GEMM_RING_ENTRY)};
+                                         PROJ_GEMM_RING_VARIANTS(PROJ_GEMM_RING_ENTRY)
+                                             PROJ_GEMM_RING32_VARIANTS(PROJ_GEMM_RING32_ENTRY)};
 const int kNumGemmVariants = sizeof(kGemmVariants) / sizeof(kGemmVariants[0]);
 #endif
 

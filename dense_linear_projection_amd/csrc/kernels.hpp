@@ -21,6 +21,7 @@ extern const int kNumStreamVariants;
 struct GemmVariant {
     const char *family;
     int bm, bn, bk, kmult, waves_m, waves_n, group_m;  // kmult: K must be a multiple of it
+    int64_t kmax;  // largest K the kernel addresses (0: no limit)
     hipError_t (*launch)(const Args &, hipStream_t);
     hipError_t (*prepare)();  // one-time function attributes (LDS size)
 };

@@ -160,6 +160,7 @@ std::vector<Candidate> candidates(const Key &k) {
         for (int i = 0; i < kNumGemmVariants; ++i) {
             const GemmVariant &v = kGemmVariants[i];
             if (k.K % v.kmult != 0) continue;
+            if (v.kmax > 0 && k.K > v.kmax) continue;
             out.push_back({KIND_GEMM, i, 1, gemm_name(v)});
         }
     }
