@@ -41,8 +41,9 @@ LLC_BYTES = 256 << 20          # last-level (Infinity) cache
 # are stale once any of its files changes)
 FAMILY_SOURCES = {
     "stream_kernel": ["stream.hip", "common.hpp"],
+    "gemm_pp_kernel": ["gemm.hip", "common.hpp"],
+    "gemm_ring32_kernel": ["gemm.hip", "common.hpp"],
     "gemm_kernel": ["gemm.hip", "common.hpp"],
-    "gemm_pipe_kernel": ["gemm.hip", "common.hpp"],
 }
 
 

@@ -186,6 +186,7 @@ Candidate default_candidate(const Key &k) {
             if (((k.N + 31) / 32) * x.splits >= 256 || x.splits == 8) return x;
         }
     }
+    if (const Candidate *g = find("gemmpp_256x256x32_w4x2_g4")) return *g;
     if (const Candidate *g = find("gemm_256x256x64_w2x2_g4")) return *g;
     for (const Candidate &x : c)
         if (x.kind == KIND_GEMM) return x;
