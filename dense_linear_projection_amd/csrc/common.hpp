@@ -100,6 +100,12 @@ __device__ __forceinline__ void dma16(const void *src, void *lds_wave_base) {
     __builtin_amdgcn_global_load_lds(src, lds_wave_base, 16, 0, 0);
 }
 
+// The same copy with the non-temporal (streaming) cache hint: for data read
+// exactly once, so that it does not push reused data out of L2.
+__device__ __forceinline__ void dma16_nt(const void *src, void *lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(src, lds_wave_base, 16, 0, 2);
+}
+
 // Raw buffer resource over [base, base + bytes): loads at offsets at or past
 // `bytes` return zero instead of touching memory.  Word 3 is the gfx9 raw
 // (untyped, unswizzled) buffer format.

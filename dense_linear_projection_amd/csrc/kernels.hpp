@@ -11,6 +11,7 @@ namespace proj {
 struct StreamVariant {
     const char *family;
     int mt, nt, waves, kc, depth;
+    int wnt;  // W copies carry the non-temporal (streaming) cache hint
     hipError_t (*launch)(const Args &, int splits, hipStream_t);
     hipError_t (*prepare)();  // one-time function attributes (LDS size)
 };

@@ -126,7 +126,8 @@ int mt_for(int64_t M) {
 
 std::string stream_name(const StreamVariant &v, int S) {
     char b[96];
-    snprintf(b, sizeof b, "stream_mt%d_nt%d_w%d_k%d_d%d_s%d", v.mt, v.nt, v.waves, v.kc, v.depth, S);
+    snprintf(b, sizeof b, "stream_mt%d_nt%d_w%d_k%d_d%d%s_s%d", v.mt, v.nt, v.waves, v.kc, v.depth,
+             v.wnt ? "_wnt" : "", S);
     return b;
 }
 
@@ -182,7 +183,7 @@ Candidate default_candidate(const Key &k) {
         for (const Candidate &x : c) {
             if (x.kind != KIND_STREAM) continue;
             const StreamVariant &v = kStreamVariants[x.variant];
-            if (v.nt != 2 || v.kc != 128 || v.depth != 5 || v.waves != 4) continue;
+            if (v.nt != 2 || v.kc != 128 || v.depth != 5 || v.waves != 4 || v.wnt) continue;
             if (((k.N + 31) / 32) * x.splits >= 256 || x.splits == 8) return x;
         }
     }

@@ -31,6 +31,9 @@
 //   * LDS rows hold 16-byte chunks at position chunk ^ (row & 15), so the 16
 //     rows read by one fragment load fall on distinct banks; the DMA writes
 //     lane i to position i, so the XOR picks each lane's global source;
+//   * optionally (WNT) the W copies carry the non-temporal cache hint: W is
+//     read once, and streaming it past L2 keeps the X rows, which every
+//     workgroup re-reads, resident there (it pays when X is large, M = 64);
 //   * workgroups walk their stages starting at a tile-dependent rotation, so
 //     at any moment the machine's reads are spread over all of K rather than
 //     all hitting the same column offset of every power-of-two-strided row.
@@ -76,7 +79,7 @@ struct StreamCfg {
     static_assert(D >= 2, "ring depth");
 };
 
-template <int MT, int NT, int WAVES, int KC, int D>
+template <int MT, int NT, int WAVES, int KC, int D, int WNT>
 __global__ __launch_bounds__(WAVES * 64) void stream_kernel(Args a, int S) {
     using C = StreamCfg<MT, NT, WAVES, KC, D>;
     extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -121,8 +124,12 @@ __global__ __launch_bounds__(WAVES * 64) void stream_kernel(Args a, int S) {
 #pragma unroll
         for (int j = 0; j < C::PERW; ++j) {
             const bool ok = i < nst && src[j] != nullptr && k0 + kofs[j] < K;
-            dma16(ok ? static_cast<const void *>(src[j] + k0) : static_cast<const void *>(a.zeros),
-                  slot + (wave + j * WAVES) * 1024);
+            const void *from = ok ? static_cast<const void *>(src[j] + k0) : static_cast<const void *>(a.zeros);
+            char *to = slot + (wave + j * WAVES) * 1024;
+            if (WNT && (wave + j * WAVES) * C::RPI < C::NR)
+                dma16_nt(from, to);  // a block of W rows (wave-uniform branch)
+            else
+                dma16(from, to);
         }
     };
 
@@ -215,33 +222,35 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(Args a, int S) {
 }
 
 // ---------------------------------------------------------------- registry
-#define PROJ_STREAM_VARIANTS(X)                                                                  \
-    X(1, 1, 8, 256, 4) X(1, 2, 8, 256, 4) X(1, 2, 8, 256, 3) X(1, 4, 8, 256, 3)                  \
-    X(1, 1, 4, 128, 9) X(1, 1, 4, 128, 6) X(1, 2, 4, 128, 5) X(1, 2, 4, 128, 7)                  \
-    X(1, 2, 2, 128, 5) X(1, 4, 4, 128, 4) X(1, 4, 4, 128, 3)                                      \
-    X(2, 2, 8, 256, 4) X(2, 2, 4, 128, 5) X(2, 4, 4, 128, 4)                                      \
-    X(4, 2, 8, 256, 3) X(4, 4, 8, 256, 2) X(4, 4, 4, 128, 4) X(4, 4, 4, 128, 5)                  \
-    X(4, 2, 4, 128, 4) X(4, 2, 4, 128, 6) X(4, 7, 4, 128, 3)
+#define PROJ_STREAM_VARIANTS(X)                                                                           \
+    X(1, 1, 8, 256, 4, 0) X(1, 2, 8, 256, 4, 0) X(1, 2, 8, 256, 3, 0) X(1, 4, 8, 256, 3, 0)                \
+    X(1, 1, 4, 128, 9, 0) X(1, 1, 4, 128, 6, 0) X(1, 2, 4, 128, 5, 0) X(1, 2, 4, 128, 7, 0)                \
+    X(1, 2, 2, 128, 5, 0) X(1, 4, 4, 128, 4, 0) X(1, 4, 4, 128, 3, 0)                                      \
+    X(2, 2, 8, 256, 4, 0) X(2, 2, 4, 128, 5, 0) X(2, 4, 4, 128, 4, 0)                                      \
+    X(4, 2, 8, 256, 3, 0) X(4, 4, 8, 256, 2, 0) X(4, 4, 4, 128, 4, 0) X(4, 4, 4, 128, 5, 0)                \
+    X(4, 2, 4, 128, 4, 0) X(4, 2, 4, 128, 6, 0) X(4, 7, 4, 128, 3, 0)                                      \
+    X(1, 2, 4, 128, 5, 1) X(1, 1, 8, 256, 4, 1) X(2, 4, 4, 128, 4, 1)                                      \
+    X(4, 7, 4, 128, 3, 1) X(4, 4, 4, 128, 4, 1) X(4, 2, 4, 128, 6, 1)
 
-#define PROJ_STREAM_INST(MT, NT, WV, KC, D) \
-    template __global__ void stream_kernel<MT, NT, WV, KC, D>(Args, int);
+#define PROJ_STREAM_INST(MT, NT, WV, KC, D, WNT) \
+    template __global__ void stream_kernel<MT, NT, WV, KC, D, WNT>(Args, int);
 PROJ_STREAM_VARIANTS(PROJ_STREAM_INST)
 
 #ifndef __HIP_DEVICE_COMPILE__
-template <int MT, int NT, int WV, int KC, int D>
+template <int MT, int NT, int WV, int KC, int D, int WNT>
 static hipError_t prepare_stream() {
-    auto fn = stream_kernel<MT, NT, WV, KC, D>;
+    auto fn = stream_kernel<MT, NT, WV, KC, D, WNT>;
     return hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
                                StreamCfg<MT, NT, WV, KC, D>::LDS);
 }
 
-template <int MT, int NT, int WV, int KC, int D>
+template <int MT, int NT, int WV, int KC, int D, int WNT>
 static hipError_t launch_stream(const Args &a, int S, hipStream_t st) {
     const int64_t tiles = (a.N + 16 * NT - 1) / (16 * NT);
     const int64_t grid = tiles * S;
     if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     constexpr int lds_bytes = StreamCfg<MT, NT, WV, KC, D>::LDS;
-    hipLaunchKernelGGL((stream_kernel<MT, NT, WV, KC, D>), dim3(static_cast<unsigned>(grid)), dim3(WV * 64),
+    hipLaunchKernelGGL((stream_kernel<MT, NT, WV, KC, D, WNT>), dim3(static_cast<unsigned>(grid)), dim3(WV * 64),
                        lds_bytes, st, a, S);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || S == 1) return e;
@@ -250,8 +259,8 @@ static hipError_t launch_stream(const Args &a, int S, hipStream_t st) {
     return hipGetLastError();
 }
 
-#define PROJ_STREAM_ENTRY(MT, NT, WV, KC, D) \
-    {"stream", MT, NT, WV, KC, D, &launch_stream<MT, NT, WV, KC, D>, &prepare_stream<MT, NT, WV, KC, D>},
+#define PROJ_STREAM_ENTRY(MT, NT, WV, KC, D, WNT) \
+    {"stream", MT, NT, WV, KC, D, WNT, &launch_stream<MT, NT, WV, KC, D, WNT>, &prepare_stream<MT, NT, WV, KC, D, WNT>},
 const StreamVariant kStreamVariants[] = {PROJ_STREAM_VARIANTS(PROJ_STREAM_ENTRY)};
 const int kNumStreamVariants = sizeof(kStreamVariants) / sizeof(kStreamVariants[0]);
 #endif
