@@ -83,14 +83,17 @@ def load_traffic(workload_name: str):
                  + c["write_kib_per_dispatch"] * 1024 * c["write_scale"], 1)
 
 
-def _pmc_per_dispatch(run_dir: str, counter: str, name_part: str, skip_first: int = 0):
+def _pmc_per_dispatch(run_dir: str, counter: str, name_part: str, skip_first: int = 0, grid: int = 0):
     """Mean of one counter over the dispatches of kernels whose name holds
-    name_part, from a rocprofv3 --pmc CSV output directory."""
+    name_part (and, if grid > 0, whose grid has that many work-items), from a
+    rocprofv3 --pmc CSV output directory."""
     import csv
     vals = {}
     for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
         with open(path) as f:
             for r in csv.DictReader(f):
+                if grid and int(r["Grid_Size"]) != grid:
+                    continue
                 if name_part in r["Kernel_Name"] and r["Counter_Name"] == counter:
                     key = (path, r["Dispatch_Id"])
                     vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
@@ -106,14 +109,17 @@ def ingest_counters(args) -> int:
     import synth
     w = synth.WORKLOADS[args.workload]
     kern = args.kernel_name
-    fetch, nf = _pmc_per_dispatch(args.ingest[0], "FETCH_SIZE", kern, skip_first=0)
-    write, nw = _pmc_per_dispatch(args.ingest[1], "WRITE_SIZE", kern, skip_first=0)
+    # the planned launch only: the tuner also runs this kernel with other
+    # split counts (other grids, extra partial-sum writes)
+    fetch, nf = _pmc_per_dispatch(args.ingest[0], "FETCH_SIZE", kern, grid=args.grid)
+    write, nw = _pmc_per_dispatch(args.ingest[1], "WRITE_SIZE", kern, grid=args.grid)
     cfetch, _ = _pmc_per_dispatch(args.ingest[2], "FETCH_SIZE", "copy")
     cwrite, _ = _pmc_per_dispatch(args.ingest[3], "WRITE_SIZE", "copy")
     copy_bytes = COPY_BYTES
     out = {
         "workload": w.name,
         "kernel_name_part": kern,
+        "grid_work_items": args.grid,
         "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
         "dispatches": [nf, nw],
         "copy_bytes": copy_bytes,
@@ -193,6 +199,8 @@ def main() -> int:
     ap.add_argument("--ingest", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="write profiles/counters_<workload>.json from rocprofv3 --pmc outputs")
     ap.add_argument("--kernel-name", default="stream_kernel", help="kernel name part for --ingest")
+    ap.add_argument("--grid", type=int, default=0,
+                    help="for --ingest: work-items of the planned launch (0: every dispatch of the kernel)")
     args = ap.parse_args()
     if args.ingest:
         return ingest_counters(args)
