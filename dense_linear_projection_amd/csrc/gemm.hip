@@ -185,11 +185,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(Args a) {
 //     t-1), the rest of stage t+3 in the first half of stage t, so a slot is
 //     refilled three stages before it is read and the address unit sees an
 //     even load;
-//   * rows of 64 bytes hold 16-byte chunks at position chunk ^ ((row >> 1) & 3):
-//     a 16-byte LDS read is served eight lanes at a time over 128 bytes of
-//     banks, and eight consecutive rows then cover all eight 16-byte bank
-//     groups; the DMA writes lane i to position i, so the XOR picks each
-//     lane's source.
+//   * rows of 64 bytes hold 16-byte chunks at position chunk ^ ((row >> 2) & 3).
+//     For the 32x32 fragment read (lanes 0..31 one chunk of 32 rows, lanes
+//     32..63 the next chunk of the same rows) this is the swizzle with no
+//     LDS bank conflicts: measured with SQ_LDS_BANK_CONFLICT on each
+//     candidate pattern, (row >> 1) & 3 costs 4 conflict cycles per read here
+//     (it is the conflict-free one for 16-row fragments) and no swizzle 12.
+//     The DMA writes lane i to position i, so the XOR picks each lane's
+//     source.
 // Scheduling-group barriers place each group's memory instructions one at a
 // time between its matrix ops; a memory instruction issued right behind
 // another stalls the SIMD's matrix pipe, one issued between two matrix ops
@@ -241,13 +244,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int64_t m0 = tm * BM, n0 = tn * BN;
 
     // DMA: block b (16 rows) of a stage is one 1 KB copy; lane l fills row
-    // 16b + l/4, position l%4, which holds chunk (l%4) ^ ((l/8)%4).  The
+    // 16b + l/4, position l%4, which holds chunk (l%4) ^ ((l/16)%4).  The
     // first A_BLK/NW copies of each wave are X blocks, the rest W blocks.
     // Each operand is read through a buffer resource over the tile's valid
     // rows: rows past M or N read as zero, the per-lane offset is fixed for
     // the whole loop and the k offset is a scalar.
     const int drow = lane >> 2;
-    const int dchunk = (lane & 3) ^ ((lane >> 3) & 3);
+    const int dchunk = (lane & 3) ^ ((lane >> 4) & 3);
     const int64_t rows_a = (M - m0) < BM ? (M - m0) : BM;
     const int64_t rows_b = (N - n0) < BN ? (N - n0) : BN;
     const __amdgpu_buffer_rsrc_t rsrc_a = buffer_rsrc(a.X + m0 * K, static_cast<uint32_t>(rows_a * K * 2));
@@ -282,7 +285,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // fragment of 32 rows starting at row0 (a multiple of 32), k-half h:
     // lane l reads row row0 + l%32, chunk 2h + l/32
     const int fr = lane & 31, fq = lane >> 5;
-    const int sw = (fr >> 1) & 3;
+    const int sw = (fr >> 2) & 3;
     auto frag = [&](const char *base, int row0, int h) -> bf16x8 {
         return *reinterpret_cast<const bf16x8 *>(base + (row0 + fr) * ROWB + (((2 * h + fq) ^ sw) << 4));
     };
@@ -516,7 +519,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // stage of this workgroup and holds that tile's buffer resources
     // (stages past the last tile read through the empty resource)
     const int drow = lane >> 2;
-    const int dchunk = (lane & 3) ^ ((lane >> 3) & 3);
+    const int dchunk = (lane & 3) ^ ((lane >> 4) & 3);
     uint32_t voff[PERW];
 #pragma unroll
     for (int j = 0; j < PERW; ++j) {
@@ -582,7 +585,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     };
     zero_acc();
 
-    const int sw = (fr >> 1) & 3;
+    const int sw = (fr >> 2) & 3;
     auto frag = [&](const char *base, int row0, int h) -> bf16x8 {
         return *reinterpret_cast<const bf16x8 *>(base + (row0 + fr) * ROWB + (((2 * h + fq) ^ sw) << 4));
     };
@@ -770,7 +773,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // other wave's memory instructions issue, instead of one wave interleaving
 // both.
 //   * tile 256 x BN, BK = 32 stages in a D = 5 slot LDS ring (64-byte rows,
-//     16-byte chunks at position chunk ^ ((row >> 1) & 3), as in the ring
+//     16-byte chunks at position chunk ^ ((row >> 2) & 3), as in the ring
 //     kernels); wave w owns rows 64 (w / 2) .. +63 and columns
 //     (BN / 2) (w % 2) .. +BN/2-1: 2 x FN blocks of 32 x 32;
 //   * group 0 reads stage t in phase 2t and multiplies in phase 2t+1;
@@ -816,10 +819,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     // DMA: copy j of a wave is 1 KB block wave + 8 j of the stage (blocks
     // 0..15 hold X rows, the rest W rows); lane l fills row 16b + l/4,
-    // position l%4, holding chunk (l%4) ^ ((l/8)%4).
+    // position l%4, holding chunk (l%4) ^ ((l/16)%4).
     constexpr int NCMAX = (TOTAL + NW - 1) / NW;
     const int drow = lane >> 2;
-    const int dchunk = (lane & 3) ^ ((lane >> 3) & 3);
+    const int dchunk = (lane & 3) ^ ((lane >> 4) & 3);
     const int64_t rows_a = (M - m0) < BM ? (M - m0) : BM;
     const int64_t rows_b = (N - n0) < BN ? (N - n0) : BN;
     const __amdgpu_buffer_rsrc_t rsrc_a = buffer_rsrc(a.X + m0 * K, static_cast<uint32_t>(rows_a * K * 2));
@@ -849,7 +852,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
     const int fr = lane & 31, fq = lane >> 5;
-    const int sw = (fr >> 1) & 3;
+    const int sw = (fr >> 2) & 3;
     auto frag = [&](const char *base, int row0, int h) -> bf16x8 {
         return *reinterpret_cast<const bf16x8 *>(base + (row0 + fr) * ROWB + (((2 * h + fq) ^ sw) << 4));
     };
