@@ -32,7 +32,6 @@
 // row (gemm_kernel) or as zeros (buffer resources of the other two) and are
 // not stored.  The planner only picks a kernel when K is a multiple of its
 // stage depth and X, W are 16-byte aligned.
-#include <atomic>
 #include <type_traits>
 #include <utility>
 
@@ -449,320 +448,6 @@ __device__ __forceinline__ void barrier_nofence() {
     asm volatile("" ::: "memory");
 }
 
-// Persistent form of the four-wave ring kernel: one workgroup per CU walks
-// tiles blockIdx.x, + gridDim.x, ... and the DMA ring runs on across tile
-// boundaries, so a tile's first stages are in flight while the previous
-// tile finishes (no per-tile prologue).  The epilogue stages the output
-// through the one ring slot that is free at that moment (the slot of the
-// tile's last stage, refilled only after the next stage's barrier), in
-// rounds of 64 rows, and writes it with 16-byte stores.  vmcnt counts loads
-// and stores together and in issue order, so for the two stages after a
-// full-tile epilogue the barrier wait allows that epilogue's NSTO stores and
-// bias loads to stay in flight: the copies the wait must cover were issued
-// before them, and the store burst drains under the next tile's work.
-// Everything else (groups, fragments, swizzle, one copy per group,
-// interleaving) is as in gemm_ring32_kernel.  Only whole tiles with bf16
-// output and a 16-byte aligned Y: the launcher sends any other call to
-// gemm_ring32_kernel with the same tile (an element-wise store path inside
-// this loop would not fit the registers).  BN = 192 only: with the 256
-// accumulators of BN = 256 the epilogue inside the loop spills.
-template <int BN, int GM>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_rp_kernel(Args a) {
-    constexpr int BM = 256, BK = 32, D = 5, WN = 2, NW = 4;
-    constexpr int TM = 128, TN = BN / 2;
-    constexpr int FM = TM / 32, FN = TN / 32;
-    constexpr int NG = 2 * FM, MID = NG / 2;
-    constexpr int ROWB = BK * 2;
-    constexpr int STAGE = (BM + BN) * ROWB;
-    constexpr int A_BLK = BM / 16, B_BLK = BN / 16;
-    constexpr int PERW = (A_BLK + B_BLK) / NW, PA = A_BLK / NW;
-    constexpr int NBG = (FN + MID - 1) / MID;
-    constexpr int PH = (PERW + 1) / 2;
-    constexpr int NC1 = (PH + MID - 1) / MID, NC2 = (PERW - PH + MID - 1) / MID;
-    constexpr int LEAD = 2 * PERW;
-    constexpr int ER = 64, NRND = BM / ER;         // epilogue rounds of ER rows
-    constexpr int CPR = BN / 8;                    // 16-byte chunks per output row
-    constexpr int EPT = ER * CPR / 256;            // 16-byte stores per thread per round
-    constexpr int NSTO = NRND * EPT + FN;          // vector memory ops of a full-tile epilogue
-    static_assert(A_BLK % NW == 0 && B_BLK % NW == 0, "copies divide over the waves");
-    static_assert(D * STAGE <= 160 * 1024, "LDS budget");
-    static_assert(ER * BN * 2 <= STAGE && (ER * CPR) % 256 == 0 && TM % ER == 0, "epilogue rounds");
-    static_assert(LEAD + NSTO <= 63 && LEAD + PH <= 63, "vmcnt range");
-    static_assert(BN % 64 == 0, "epilogue swizzle works on 64-column halves");
-    static_assert(FN >= 3 && NBG == 1 && NC1 <= 1 && NC2 <= 1, "interleave: <= 2 reads and 1 copy per group");
-
-    extern __shared__ __attribute__((aligned(16))) char lds[];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / WN, wn = wave % WN;
-    const int64_t M = a.M, N = a.N, K = a.K;
-    // tile counts and indices fit 32 bits (the launcher checks G < 2^31)
-    const int tiles_m = static_cast<int>(M / BM), tiles_n = static_cast<int>(N / BN);
-    const int G = tiles_m * tiles_n;
-    const int P = gridDim.x;
-    const int ntl = (G - static_cast<int>(blockIdx.x) + P - 1) / P;  // tiles of this workgroup (grid <= G)
-    const int KT = static_cast<int>(K / BK);                         // even, K < 2^22 (planner)
-
-    // origin of this workgroup's tile i (XCD-contiguous, GM-grouped order)
-    auto origin = [&](int i, int &m0, int &n0) {
-        int L = static_cast<int>(blockIdx.x) + i * P;
-        if (G % 8 == 0) L = (L % 8) * (G / 8) + L / 8;
-        const int per_group = GM * tiles_n;
-        const int first_m = (L / per_group) * GM;
-        const int gsz = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
-        m0 = (first_m + (L % per_group) % gsz) * BM;
-        n0 = ((L % per_group) / gsz) * BN;
-    };
-    const __amdgpu_buffer_rsrc_t rsrc_none = buffer_rsrc(a.X, 0);
-
-    // DMA: as in gemm_ring32_kernel; a cursor names the tile and k-stage of a
-    // stage of this workgroup and holds that tile's buffer resources
-    // (stages past the last tile read through the empty resource)
-    const int drow = lane >> 2;
-    const int dchunk = (lane & 3) ^ ((lane >> 4) & 3);
-    uint32_t voff[PERW];
-#pragma unroll
-    for (int j = 0; j < PERW; ++j) {
-        const int r = (j < PA ? (wave + j * NW) : (wave + (j - PA) * NW)) * 16 + drow;
-        voff[j] = static_cast<uint32_t>(r * K * 2 + dchunk * 16);
-    }
-    struct Cur {
-        int tile;
-        int kt;
-        __amdgpu_buffer_rsrc_t ra, rb;
-    };
-    auto set_rsrc = [&](Cur &c) {
-        if (c.tile < ntl) {
-            int m0, n0;
-            origin(c.tile, m0, n0);
-            c.ra = buffer_rsrc(a.X + static_cast<int64_t>(m0) * K, static_cast<uint32_t>(BM * K * 2));
-            c.rb = buffer_rsrc(a.W + static_cast<int64_t>(n0) * K, static_cast<uint32_t>(BN * K * 2));
-        } else {
-            c.ra = rsrc_none;
-            c.rb = rsrc_none;
-        }
-    };
-    auto cursor = [&](int s) {
-        Cur c;
-        c.tile = s / KT;
-        c.kt = s % KT;
-        set_rsrc(c);
-        return c;
-    };
-    auto advance = [&](Cur &c) {
-        if (++c.kt == KT) {
-            c.kt = 0;
-            ++c.tile;
-            set_rsrc(c);
-        }
-    };
-    auto copy = [&](int j, const Cur &c, int slot) {
-        const int blk = j < PA ? wave + j * NW : A_BLK + wave + (j - PA) * NW;
-        dma16_buf(j < PA ? c.ra : c.rb, voff[j], static_cast<uint32_t>(c.kt * (BK * 2)), lds + slot * STAGE + blk * 1024);
-    };
-    auto slot_add = [](int slot, int d) { return slot + d >= D ? slot + d - D : slot + d; };
-
-    // bias of a tile's columns for this lane: exactly FN single loads (zero
-    // past N or without a bias epilogue)
-    const int fr = lane & 31, fq = lane >> 5;
-    float bias[FN];
-    auto load_bias = [&](int n0) {
-        const __amdgpu_buffer_rsrc_t rb = (a.epi & 1) ? buffer_rsrc(a.bias + n0, BN * 2) : rsrc_none;
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-            bias[j] = bf16_bits_to_f32(__builtin_amdgcn_raw_buffer_load_b16(
-                rb, static_cast<uint32_t>((wn * TN + j * 32 + fr) * 2), 0, 0));
-    };
-
-    f32x16 acc[FM][FN];
-    auto zero_acc = [&]() {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-    };
-    zero_acc();
-
-    const int sw = (fr >> 2) & 3;
-    auto frag = [&](const char *base, int row0, int h) -> bf16x8 {
-        return *reinterpret_cast<const bf16x8 *>(base + (row0 + fr) * ROWB + (((2 * h + fq) ^ sw) << 4));
-    };
-
-    // compute-side tile
-    int ci = 0, cm0, cn0;
-    origin(0, cm0, cn0);
-    load_bias(cn0);  // older than every copy: complete before the first wait
-
-    // prologue: stages 0..2 and the first part of stage 3 in flight
-    Cur c3 = cursor(3), c4 = cursor(4);
-    {
-        const Cur c0 = cursor(0), c1 = cursor(1), c2 = cursor(2);
-#pragma unroll
-        for (int j = 0; j < PERW; ++j) copy(j, c0, 0);
-#pragma unroll
-        for (int j = 0; j < PERW; ++j) copy(j, c1, 1);
-#pragma unroll
-        for (int j = 0; j < PERW; ++j) copy(j, c2, 2);
-#pragma unroll
-        for (int j = 0; j < PH; ++j) copy(j, c3, 3);
-        wait_vm<2 * PERW + PH>();
-        __syncthreads();
-    }
-
-    bf16x8 b0e[FN], b0o[FN], b1[FN], a0e[NG + 2], a0o[NG + 2];
-    {
-        const char *sa = lds, *sb = sa + BM * ROWB;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) b0e[j] = frag(sb, wn * TN + j * 32, 0);
-        a0e[0] = frag(sa, wm * TM, 0);
-        a0e[1] = frag(sa, wm * TM + 32, 0);
-        lds_wait_all();
-    }
-
-    int relax = 0;  // stages left whose barrier wait allows an epilogue in flight
-    auto stage = [&](int slot, bf16x8(&bc)[FN], bf16x8(&bn)[FN], bf16x8(&ac)[NG + 2], bf16x8(&an)[NG + 2]) {
-        const char *sa = lds + slot * STAGE, *sb = sa + BM * ROWB;
-        const char *na = lds + slot_add(slot, 1) * STAGE, *nb = na + BM * ROWB;
-        const int slot3 = slot_add(slot, 3), slot_last = slot_add(slot, D - 1);
-#pragma unroll
-        for (int g = 0; g < NG; ++g) {
-            const int h = g / FM, i = g % FM;
-            if (g == MID) {
-                if (relax > 0)
-                    wait_vm<LEAD + NSTO>();
-                else
-                    wait_vm<LEAD>();
-                lds_wait_all();
-                __builtin_amdgcn_s_barrier();
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            if (g == MID)
-                lds_wait_keep<0>();
-            else
-                lds_wait_keep<1 + NBG>();
-            const int gn = g + 2;
-            if (gn < NG)
-                ac[gn] = frag(sa, wm * TM + (gn % FM) * 32, gn / FM);
-            else
-                an[gn - NG] = frag(na, wm * TM + (gn - NG) * 32, 0);
-            const int q0 = (g % MID) * NBG;
-#pragma unroll
-            for (int q = q0; q < q0 + NBG && q < FN; ++q) {
-                if (g < MID)
-                    b1[q] = frag(sb, wn * TN + q * 32, 1);
-                else
-                    bn[q] = frag(nb, wn * TN + q * 32, 0);
-            }
-            if (g >= MID) {
-                const int c0 = (g - MID) * NC1;
-#pragma unroll
-                for (int c = c0; c < c0 + NC1 && c < PH; ++c) copy(c, c4, slot_last);
-            } else {
-                const int c0 = PH + g * NC2;
-#pragma unroll
-                for (int c = c0; c < c0 + NC2 && c < PERW; ++c) copy(c, c3, slot3);
-            }
-#pragma unroll
-            for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16(ac[g], h == 0 ? bc[j] : b1[j], acc[i][j]);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, FN - 3, 0);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        c3 = c4;
-        advance(c4);
-        if (relax > 0) --relax;
-    };
-
-    // epilogue of the compute-side tile; free_slot held its last stage
-    auto epilogue = [&](int free_slot) {
-        lds_wait_all();
-        barrier_nofence();  // no wave still reads free_slot
-        const int epi = a.epi;  // bias[] is already 0 without a bias epilogue
-        {
-            uint16_t *eb = reinterpret_cast<uint16_t *>(lds + free_slot * STAGE);
-#pragma unroll
-            for (int r = 0; r < NRND; ++r) {
-                // rows ER*r .. +ER-1 of the tile belong to the waves with wm = r*ER/TM
-                if (wm == r * ER / TM) {
-                    constexpr int BPR = ER / 32;  // 32-row blocks per round
-                    // bias (0 without one), then GELU if asked; the branch is
-                    // outside the loops so each copy is straight-line code
-                    auto put = [&](auto gelu) {
-#pragma unroll
-                        for (int j = 0; j < FN; ++j) {
-                            uint16_t *cb = eb + 4 * fq * BN + ((wn * TN + j * 32 + fr) ^ (fq << 5));
-#pragma unroll
-                            for (int ii = 0; ii < BPR; ++ii)
-#pragma unroll
-                                for (int v = 0; v < 16; ++v) {
-                                    float x = acc[(r * BPR) % FM + ii][j][v] + bias[j];
-                                    if constexpr (decltype(gelu)::value) x = gelu_tanh_fast(x);
-                                    cb[(ii * 32 + 8 * (v / 4) + (v % 4)) * BN] = f32_to_bf16_bits(x);
-                                }
-                            __builtin_amdgcn_sched_barrier(0);  // one column block at a time: few live values
-                        }
-                    };
-                    if (epi & 2)
-                        put(std::true_type{});
-                    else
-                        put(std::false_type{});
-                }
-                lds_wait_all();
-                barrier_nofence();
-                u32x4 val[EPT];
-#pragma unroll
-                for (int p = 0; p < EPT; ++p) {
-                    const int c = tid + 256 * p, row = c / CPR, ch = c % CPR;
-                    val[p] = *reinterpret_cast<const u32x4 *>(eb + row * BN + ((ch * 8) ^ (((row >> 2) & 1) << 5)));
-                }
-#pragma unroll
-                for (int p = 0; p < EPT; ++p) {
-                    const int c = tid + 256 * p, row = c / CPR, ch = c % CPR;
-                    *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.Y) + static_cast<int64_t>(cm0 + r * ER + row) * N +
-                                               cn0 + ch * 8) = val[p];
-                }
-                if (r + 1 < NRND) {
-                    lds_wait_all();
-                    barrier_nofence();  // the next round overwrites the staging rows
-                }
-            }
-            relax = 2;
-        }
-        ++ci;
-        if (ci < ntl) {
-            origin(ci, cm0, cn0);
-            load_bias(cn0);
-        } else {
-            relax = 0;
-        }
-        zero_acc();
-    };
-
-    // KT is even: tiles end on the second stage of a pair
-    int slot = 0, ktc = 0;
-    for (int q = 0; q < ntl * KT; q += 2) {
-        stage(slot, b0e, b0o, a0e, a0o);
-        slot = slot_add(slot, 1);
-        stage(slot, b0o, b0e, a0o, a0e);
-        const int done_slot = slot;
-        slot = slot_add(slot, 1);
-        ktc += 2;
-        if (ktc == KT) {
-            ktc = 0;
-            epilogue(done_slot);
-        }
-    }
-    // copies past the last stage (empty resource) still write LDS
-    wait_vm<0>();
-}
-
 // Eight-wave "ping-pong" GEMM.  Waves w and w+4 of a workgroup share a SIMD
 // (the dispatcher places wave w on SIMD w mod 4 in a fixed rotation), so the
 // workgroup is two groups of four waves, one wave of each group per SIMD.
@@ -982,10 +667,6 @@ PROJ_GEMM_VARIANTS(PROJ_GEMM_INST)
 #define PROJ_GEMM_RING32_INST(BN, GM) template __global__ void gemm_ring32_kernel<BN, GM>(Args);
 PROJ_GEMM_RING32_VARIANTS(PROJ_GEMM_RING32_INST)
 
-#define PROJ_GEMM_RP_VARIANTS(X) X(192, 4)
-#define PROJ_GEMM_RP_INST(BN, GM) template __global__ void gemm_rp_kernel<BN, GM>(Args);
-PROJ_GEMM_RP_VARIANTS(PROJ_GEMM_RP_INST)
-
 #define PROJ_GEMM_PP_VARIANTS(X) X(256, 4) X(256, 8) X(192, 4)
 #define PROJ_GEMM_PP_INST(BN, GM) template __global__ void gemm_pp_kernel<BN, GM>(Args);
 PROJ_GEMM_PP_VARIANTS(PROJ_GEMM_PP_INST)
@@ -1031,45 +712,6 @@ static hipError_t launch_gemm_ring32(const Args &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-// Number of CUs of the current device, read once (the persistent kernel's
-// grid); all devices a process drives here are the same part.
-static int device_cus() {
-    static std::atomic<int> cus{0};
-    int n = cus.load(std::memory_order_relaxed);
-    if (n == 0) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-        cus.store(n, std::memory_order_relaxed);
-    }
-    return n;
-}
-
-template <int BN, int GM>
-static hipError_t prepare_gemm_rp() {
-    device_cus();
-    auto fn = gemm_rp_kernel<BN, GM>;
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
-                               5 * (256 + BN) * 64);
-}
-
-template <int BN, int GM>
-static hipError_t launch_gemm_ring32(const Args &a, hipStream_t st);
-
-template <int BN, int GM>
-static hipError_t launch_gemm_rp(const Args &a, hipStream_t st) {
-    const int64_t G = ((a.M + 255) / 256) * ((a.N + BN - 1) / BN);
-    if (G <= 0 || G > 0x7fffffff) return hipErrorInvalidConfiguration;
-    if (a.M > 0x7fffffff || a.N > 0x7fffffff || G * ((a.K + 31) / 32) > 0x7fffffff || a.M % 256 != 0 || a.N % BN != 0 || a.N % 8 != 0 || a.out != OUT_BF16 ||
-        reinterpret_cast<uintptr_t>(a.Y) % 16 != 0)
-        return launch_gemm_ring32<BN, GM>(a, st);  // not whole aligned tiles
-    const int64_t grid = G < device_cus() ? G : device_cus();
-    constexpr int lds_bytes = 5 * (256 + BN) * 64;
-    hipLaunchKernelGGL((gemm_rp_kernel<BN, GM>), dim3(static_cast<unsigned>(grid)), dim3(256), lds_bytes, st, a);
-    return hipGetLastError();
-}
-
 template <int BN, int GM>
 static hipError_t prepare_gemm_pp() {
     auto fn = gemm_pp_kernel<BN, GM>;
@@ -1090,12 +732,10 @@ static hipError_t launch_gemm_pp(const Args &a, hipStream_t st) {
     {"gemm", BM, BN, 64, 64, WM, WN, GM, 0, &launch_gemm<BM, BN, 64, WM, WN, GM>, &prepare_gemm<BM, BN, 64, WM, WN, GM>},
 #define PROJ_GEMM_RING32_ENTRY(BN, GM) \
     {"gemmring32", 256, BN, 32, 64, 2, 2, GM, kRingMaxK, &launch_gemm_ring32<BN, GM>, &prepare_gemm_ring32<BN, GM>},
-#define PROJ_GEMM_RP_ENTRY(BN, GM) \
-    {"gemmrp", 256, BN, 32, 64, 2, 2, GM, kRingMaxK, &launch_gemm_rp<BN, GM>, &prepare_gemm_rp<BN, GM>},
 #define PROJ_GEMM_PP_ENTRY(BN, GM) \
     {"gemmpp", 256, BN, 32, 32, 4, 2, GM, kRingMaxK, &launch_gemm_pp<BN, GM>, &prepare_gemm_pp<BN, GM>},
 const GemmVariant kGemmVariants[] = {PROJ_GEMM_VARIANTS(PROJ_GEMM_ENTRY) PROJ_GEMM_RING32_VARIANTS(PROJ_GEMM_RING32_ENTRY)
-                                         PROJ_GEMM_RP_VARIANTS(PROJ_GEMM_RP_ENTRY) PROJ_GEMM_PP_VARIANTS(PROJ_GEMM_PP_ENTRY)};
+                                         PROJ_GEMM_PP_VARIANTS(PROJ_GEMM_PP_ENTRY)};
 const int kNumGemmVariants = sizeof(kGemmVariants) / sizeof(kGemmVariants[0]);
 #endif
 

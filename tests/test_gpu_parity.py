@@ -64,45 +64,6 @@ def test_every_candidate_bit_exact_on_integers(ctx, shape):
                     name, epi, out, bad[0], u[tuple(bad[0])], r[tuple(bad[0])])
 
 
-# Whole 256 x 192 tiles and more tiles than CUs: the persistent GEMM runs its
-# own path (one workgroup per CU walking several tiles, its DMA ring running
-# across tile boundaries) instead of handing the call to the ring kernel.
-# 3840 x 3840 is 300 tiles: some workgroups take two tiles, the rest one;
-# K = 128 is four stages per tile.
-def persistent_candidates(M, N, K, epi, out):
-    names = candidate_names(M, N, K, epi, out)
-    idx = [i for i, n in enumerate(names) if n.startswith("gemmrp")]
-    assert idx, names
-    return idx
-
-
-def test_persistent_gemm_bit_exact_on_integers(ctx):
-    M, N, K = 3840, 3840, 128
-    X = synth.integer_bf16((M, K), -8, 8, 41)
-    W = synth.integer_bf16((N, K), -8, 8, 42)
-    b = synth.integer_bf16((N,), -64, 64, 43)
-    Xd, Wd, bd = dev_bf16(X), dev_bf16(W), dev_bf16(b)
-    for epi in (oracle.EPI_NONE, oracle.EPI_BIAS):
-        r, _ = oracle.reference(X, W, b if epi & 1 else None, epi, oracle.OUT_BF16)
-        for i in persistent_candidates(M, N, K, epi, oracle.OUT_BF16):
-            u = run_candidate(ctx, i, Xd, Wd, bd, epi, M, N, K, oracle.OUT_BF16)
-            bad = np.argwhere(u != r)
-            assert bad.size == 0, "epi=%d: first mismatch at %s: %r vs %r" % (
-                epi, bad[0], u[tuple(bad[0])], r[tuple(bad[0])])
-
-
-def test_persistent_gemm_random_bias_gelu(ctx):
-    M, N, K = 4352, 3072, 256   # 272 tiles
-    X, W, b = synth.make_inputs(M, N, K, True, 44)
-    Xd, Wd, bd = dev_bf16(X), dev_bf16(W), dev_bf16(b)
-    epi = oracle.EPI_BIAS_GELU
-    r, _ = oracle.reference(X, W, b, epi, oracle.OUT_BF16)
-    for i in persistent_candidates(M, N, K, epi, oracle.OUT_BF16):
-        u = run_candidate(ctx, i, Xd, Wd, bd, epi, M, N, K, oracle.OUT_BF16)
-        rep = compare.check(u, r)
-        assert rep["ok"], rep
-
-
 RAND_SHAPES = [(16, 1040, 2048), (64, 200, 1024), (17, 64, 512), (520, 384, 640)]
 
 
