@@ -121,6 +121,13 @@ __device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t vof
                                              voff, soff, 0, 0);
 }
 
+// The same copy with the non-temporal (streaming) cache hint.
+__device__ __forceinline__ void dma16_buf_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                             void *lds_wave_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_wave_base, 16,
+                                             voff, soff, 0, 2);
+}
+
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // s_waitcnt lgkmcnt(0) (vmcnt and expcnt left at their maxima), emitted as a

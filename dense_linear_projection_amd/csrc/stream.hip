@@ -39,6 +39,15 @@
 //     all hitting the same column offset of every power-of-two-strided row.
 // Chunks past K or rows past M / N read the zero page (no load leaves the
 // caller's buffers); rows past M / N are not stored.
+//
+// FAST (chosen per call when K is a multiple of KC): the copies go through
+// buffer resources over the tile's W rows and over X, with the per-lane
+// offsets fixed for the whole loop and the stage's k offset a scalar, so a
+// copy is one instruction with no vector arithmetic; rows past N or M read
+// as zero from the resource bounds, and stages past the end are still
+// issued through an empty resource, so every stage waits for the same vmcnt
+// with no branch (the general path spends most of a stage on per-lane
+// address arithmetic and on picking the wait).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -79,12 +88,13 @@ struct StreamCfg {
     static_assert(D >= 2, "ring depth");
 };
 
-template <int MT, int NT, int WAVES, int KC, int D, int WNT>
+template <int MT, int NT, int WAVES, int KC, int D, int WNT, bool FAST>
 __global__ __launch_bounds__(WAVES * 64) void stream_kernel(Args a, int S) {
     using C = StreamCfg<MT, NT, WAVES, KC, D>;
     extern __shared__ __attribute__((aligned(16))) char lds[];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tile = blockIdx.x / S, split = blockIdx.x % S;
     const int64_t K = a.K, M = a.M, N = a.N;
     const int64_t n0 = static_cast<int64_t>(tile) * C::NR;
@@ -118,18 +128,51 @@ __global__ __launch_bounds__(WAVES * 64) void stream_kernel(Args a, int S) {
             src[j] = m < M ? a.X + m * K + chunk * 8 : nullptr;
         }
     }
-    auto issue = [&](int i) {
-        char *slot = lds + (i % D) * C::STAGE;
-        const int64_t k0 = i < nst ? stage_k0(i) : 0;
+    // FAST: resources over the tile's valid W rows and over X, and each
+    // copy's byte offset within its operand
+    uint32_t wbytes = 0, xbytes = 0;
+    uint32_t voff[C::PERW];
+    if constexpr (FAST) {
+        const int64_t rows_w = (N - n0) < C::NR ? (N - n0) : C::NR;
+        wbytes = static_cast<uint32_t>(rows_w * K * 2);
+        xbytes = static_cast<uint32_t>(M * K * 2);
 #pragma unroll
         for (int j = 0; j < C::PERW; ++j) {
-            const bool ok = i < nst && src[j] != nullptr && k0 + kofs[j] < K;
-            const void *from = ok ? static_cast<const void *>(src[j] + k0) : static_cast<const void *>(a.zeros);
-            char *to = slot + (wave + j * WAVES) * 1024;
-            if (WNT && (wave + j * WAVES) * C::RPI < C::NR)
-                dma16_nt(from, to);  // a block of W rows (wave-uniform branch)
-            else
-                dma16(from, to);
+            const int row = (wave + j * WAVES) * C::RPI + lane / C::CPR;
+            const int chunk = (lane % C::CPR) ^ (row & 15);
+            const int64_t r = row < C::NR ? row : row - C::NR;
+            voff[j] = static_cast<uint32_t>((r * K + chunk * 8) * 2);
+        }
+    }
+    auto issue = [&](int i) {
+        char *slot = lds + (i % D) * C::STAGE;
+        if constexpr (FAST) {
+            const bool live = i < nst;
+            const uint32_t soff = static_cast<uint32_t>(stage_k0(live ? i : 0) * 2);
+            const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(a.W + n0 * K, live ? wbytes : 0u);
+            const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(a.X, live ? xbytes : 0u);
+#pragma unroll
+            for (int j = 0; j < C::PERW; ++j) {
+                const bool is_w = (wave + j * WAVES) * C::RPI < C::NR;  // wave-uniform
+                const __amdgpu_buffer_rsrc_t r = is_w ? rw : rx;
+                char *to = slot + (wave + j * WAVES) * 1024;
+                if (WNT && is_w)
+                    dma16_buf_nt(r, voff[j], soff, to);
+                else
+                    dma16_buf(r, voff[j], soff, to);
+            }
+        } else {
+            const int64_t k0 = i < nst ? stage_k0(i) : 0;
+#pragma unroll
+            for (int j = 0; j < C::PERW; ++j) {
+                const bool ok = i < nst && src[j] != nullptr && k0 + kofs[j] < K;
+                const void *from = ok ? static_cast<const void *>(src[j] + k0) : static_cast<const void *>(a.zeros);
+                char *to = slot + (wave + j * WAVES) * 1024;
+                if (WNT && (wave + j * WAVES) * C::RPI < C::NR)
+                    dma16_nt(from, to);  // a block of W rows (wave-uniform branch)
+                else
+                    dma16(from, to);
+            }
         }
     };
 
@@ -145,12 +188,16 @@ __global__ __launch_bounds__(WAVES * 64) void stream_kernel(Args a, int S) {
 
     for (int i = 0; i < nst; ++i) {
         // this wave's copies of stage i are done once at most
-        // min(D-2, nst-1-i) later stages are still in flight
-        wait_stages<C::PERW, D - 2>(nst - 1 - i);
+        // min(D-2, nst-1-i) later stages are still in flight (FAST: always
+        // D-2, copies past the end being issued too)
+        if constexpr (FAST)
+            wait_vm<C::PERW * (D - 2)>();
+        else
+            wait_stages<C::PERW, D - 2>(nst - 1 - i);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        if (i + D - 1 < nst) issue(i + D - 1);
+        if (FAST || i + D - 1 < nst) issue(i + D - 1);
         const char *slot = lds + (i % D) * C::STAGE;
 #pragma unroll
         for (int kk = wave % C::KS; kk < C::KS; kk += WAVES) {
@@ -232,15 +279,20 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(Args a, int S) {
     X(1, 2, 4, 128, 5, 1) X(1, 1, 8, 256, 4, 1) X(2, 4, 4, 128, 4, 1)                                      \
     X(4, 7, 4, 128, 3, 1) X(4, 4, 4, 128, 4, 1) X(4, 2, 4, 128, 6, 1)
 
-#define PROJ_STREAM_INST(MT, NT, WV, KC, D, WNT) \
-    template __global__ void stream_kernel<MT, NT, WV, KC, D, WNT>(Args, int);
+#define PROJ_STREAM_INST(MT, NT, WV, KC, D, WNT)                                  \
+    template __global__ void stream_kernel<MT, NT, WV, KC, D, WNT, false>(Args, int); \
+    template __global__ void stream_kernel<MT, NT, WV, KC, D, WNT, true>(Args, int);
 PROJ_STREAM_VARIANTS(PROJ_STREAM_INST)
 
 #ifndef __HIP_DEVICE_COMPILE__
 template <int MT, int NT, int WV, int KC, int D, int WNT>
 static hipError_t prepare_stream() {
-    auto fn = stream_kernel<MT, NT, WV, KC, D, WNT>;
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+    auto slow = stream_kernel<MT, NT, WV, KC, D, WNT, false>;
+    auto fast = stream_kernel<MT, NT, WV, KC, D, WNT, true>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(slow), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       StreamCfg<MT, NT, WV, KC, D>::LDS);
+    if (e != hipSuccess) return e;
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(fast), hipFuncAttributeMaxDynamicSharedMemorySize,
                                StreamCfg<MT, NT, WV, KC, D>::LDS);
 }
 
@@ -250,8 +302,14 @@ static hipError_t launch_stream(const Args &a, int S, hipStream_t st) {
     const int64_t grid = tiles * S;
     if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     constexpr int lds_bytes = StreamCfg<MT, NT, WV, KC, D>::LDS;
-    hipLaunchKernelGGL((stream_kernel<MT, NT, WV, KC, D, WNT>), dim3(static_cast<unsigned>(grid)), dim3(WV * 64),
-                       lds_bytes, st, a, S);
+    // the buffer-resource path needs whole stages and 32-bit operand offsets
+    const bool fast = a.K % KC == 0 && a.M * a.K * 2 < (int64_t{1} << 32) && 16 * NT * a.K * 2 < (int64_t{1} << 32);
+    if (fast)
+        hipLaunchKernelGGL((stream_kernel<MT, NT, WV, KC, D, WNT, true>), dim3(static_cast<unsigned>(grid)),
+                           dim3(WV * 64), lds_bytes, st, a, S);
+    else
+        hipLaunchKernelGGL((stream_kernel<MT, NT, WV, KC, D, WNT, false>), dim3(static_cast<unsigned>(grid)),
+                           dim3(WV * 64), lds_bytes, st, a, S);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || S == 1) return e;
     const int64_t blocks = (a.M * a.N + 255) / 256;

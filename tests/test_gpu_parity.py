@@ -37,6 +37,7 @@ def candidate_names(M, N, K, epi, out, aligned=True):
 INT_SHAPES = [
     (16, 200, 256),    # N not a multiple of 16
     (5, 77, 96),       # M < 16
+    (5, 77, 512),      # M < 16, whole stages (buffer-resource copy path)
     (33, 130, 264),    # 3 m-tiles of 16, K % 32 == 8 (partial k-step)
     (64, 256, 1024),
     (1, 48, 4104),     # one token row, K % 32 == 8, many k-steps
