@@ -56,22 +56,15 @@ def kernel_sources_hash(family: str) -> str:
     return h.hexdigest()[:16]
 
 
-def family_of(kernel_name: str) -> str:
-    for fam in FAMILY_SOURCES:
-        if kernel_name.startswith(fam.split("_kernel")[0].replace("_", "")) or fam in kernel_name:
-            return fam
-    raise ValueError("unknown kernel family for %r" % kernel_name)
-
-
 def counters_path(workload_name: str) -> str:
     return os.path.join(ROOT, "profiles", "counters_%s.json" % workload_name)
 
 
-def load_traffic(workload_name: str):
-    """HBM bytes per launch of the projection kernel, from committed
-    rocprofv3 counter runs (FETCH_SIZE and WRITE_SIZE, each scaled by what
-    the same counter reads for a plain copy of known size), if they were
-    taken on the current kernel sources; else None."""
+def load_traffic(workload_name: str, plan_kernel: str):
+    """HBM bytes per launch of the planned kernel, from committed rocprofv3
+    counter runs (FETCH_SIZE and WRITE_SIZE, each scaled by what the same
+    counter reads for a plain copy of known size), if they were taken on the
+    current kernel sources and include this plan; else None."""
     path = counters_path(workload_name)
     if not os.path.exists(path):
         return None
@@ -79,8 +72,26 @@ def load_traffic(workload_name: str):
         c = json.load(f)
     if c.get("src_hash") != kernel_sources_hash(c["family"]):
         return None
-    return round(c["fetch_kib_per_dispatch"] * 1024 * c["fetch_scale"]
-                 + c["write_kib_per_dispatch"] * 1024 * c["write_scale"], 1)
+    entry = c.get("plans", {}).get(plan_kernel)
+    return None if entry is None else round(entry["traffic_bytes_per_launch"], 1)
+
+
+def stream_plan_launch(plan: str, w):
+    """(kernel-name part, work-items) of the launch a one-pass stream plan
+    makes on workload w, e.g. stream_mt1_nt2_w4_k128_d4_wnt_s1 ->
+    ("stream_kernel<1, 2, 4, 128, 4, 1, true>", 65536)."""
+    import re
+    m = re.fullmatch(r"stream_mt(\d+)_nt(\d+)_w(\d+)_k(\d+)_d(\d+)(_wnt)?_s(\d+)", plan)
+    if m is None:
+        raise SystemExit("not a stream plan: %r" % plan)
+    mt, nt, waves, kc, d = (int(m.group(i)) for i in range(1, 6))
+    wnt, S = m.group(6) is not None, int(m.group(7))
+    if S != 1:
+        raise SystemExit("counters are taken on one-pass plans only (a split plan adds a reduction kernel)")
+    fast = w.K % kc == 0  # whole stages take the buffer-resource copy path
+    name = "stream_kernel<%d, %d, %d, %d, %d, %d, %s>" % (mt, nt, waves, kc, d, int(wnt), "true" if fast else "false")
+    tiles = -(-w.N // (16 * nt))
+    return name, tiles * S * waves * 64
 
 
 def _pmc_per_dispatch(run_dir: str, counter: str, name_part: str, skip_first: int = 0, grid: int = 0):
@@ -105,33 +116,37 @@ def _pmc_per_dispatch(run_dir: str, counter: str, name_part: str, skip_first: in
 
 def ingest_counters(args) -> int:
     """Write profiles/counters_<workload>.json from four rocprofv3 --pmc runs:
-    FETCH_SIZE and WRITE_SIZE of this bench, and of --copy-calibration."""
+    FETCH_SIZE and WRITE_SIZE of this bench, and of --copy-calibration.  The
+    plan tuner runs every candidate on cold caches, so one pair of runs holds
+    samples of each candidate plan; each plan named in --plans gets its own
+    figures, taken on its own kernel instantiation and grid."""
     import synth
     w = synth.WORKLOADS[args.workload]
-    kern = args.kernel_name
-    # the planned launch only: the tuner also runs this kernel with other
-    # split counts (other grids, extra partial-sum writes)
-    fetch, nf = _pmc_per_dispatch(args.ingest[0], "FETCH_SIZE", kern, grid=args.grid)
-    write, nw = _pmc_per_dispatch(args.ingest[1], "WRITE_SIZE", kern, grid=args.grid)
     cfetch, _ = _pmc_per_dispatch(args.ingest[2], "FETCH_SIZE", "copy")
     cwrite, _ = _pmc_per_dispatch(args.ingest[3], "WRITE_SIZE", "copy")
     copy_bytes = COPY_BYTES
+    fetch_scale, write_scale = copy_bytes / (cfetch * 1024), copy_bytes / (cwrite * 1024)
+    plans = {}
+    for plan in args.plans:
+        kern, grid = stream_plan_launch(plan, w)
+        fetch, nf = _pmc_per_dispatch(args.ingest[0], "FETCH_SIZE", kern, grid=grid)
+        write, nw = _pmc_per_dispatch(args.ingest[1], "WRITE_SIZE", kern, grid=grid)
+        traffic = fetch * 1024 * fetch_scale + write * 1024 * write_scale
+        plans[plan] = {"kernel_name_part": kern, "grid_work_items": grid,
+                       "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
+                       "dispatches": [nf, nw], "traffic_bytes_per_launch": traffic,
+                       "traffic_over_alg": traffic / w.alg_bytes()}
     out = {
         "workload": w.name,
-        "kernel_name_part": kern,
-        "grid_work_items": args.grid,
-        "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
-        "dispatches": [nf, nw],
         "copy_bytes": copy_bytes,
         "copy_fetch_kib": cfetch, "copy_write_kib": cwrite,
-        "fetch_scale": copy_bytes / (cfetch * 1024), "write_scale": copy_bytes / (cwrite * 1024),
+        "fetch_scale": fetch_scale, "write_scale": write_scale,
         "alg_bytes_per_launch": w.alg_bytes(),
-        "family": family_of(kern),
-        "src_files": FAMILY_SOURCES[family_of(kern)],
-        "src_hash": kernel_sources_hash(family_of(kern)),
+        "family": "stream_kernel",
+        "src_files": FAMILY_SOURCES["stream_kernel"],
+        "src_hash": kernel_sources_hash("stream_kernel"),
+        "plans": plans,
     }
-    out["traffic_bytes_per_launch"] = (out["fetch_kib_per_dispatch"] * 1024 * out["fetch_scale"]
-                                       + out["write_kib_per_dispatch"] * 1024 * out["write_scale"])
     with open(counters_path(w.name), "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
@@ -206,9 +221,8 @@ def main() -> int:
                     help="only run a plain copy of known size (for counter scaling)")
     ap.add_argument("--ingest", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="write profiles/counters_<workload>.json from rocprofv3 --pmc outputs")
-    ap.add_argument("--kernel-name", default="stream_kernel", help="kernel name part for --ingest")
-    ap.add_argument("--grid", type=int, default=0,
-                    help="for --ingest: work-items of the planned launch (0: every dispatch of the kernel)")
+    ap.add_argument("--plans", nargs="+", default=[],
+                    help="for --ingest: one-pass stream plans to take counters for")
     args = ap.parse_args()
     if args.ingest:
         return ingest_counters(args)
@@ -294,7 +308,7 @@ def main() -> int:
     gbs = w.alg_bytes() / sec / 1e9
     tflops = w.alg_flops() / sec / 1e12
     hbm_bound = w.M <= 64
-    traffic = load_traffic(w.name)
+    traffic = load_traffic(w.name, plan.split(" ")[0])
     if hbm_bound:
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic}

@@ -291,43 +291,70 @@ proj_status tune(proj_ctx *c, const Key &k, const Args &a, hipStream_t st, Plan 
         hipEventDestroy(e0);
         return hip_fail(c, "hipEventCreate", hipGetLastError());
     }
-    const int reps = 7;
-    float best = 1e30f;
-    int best_i = -1;
+    // one timed run of candidate i (after a cache flush where that applies);
+    // a negative time if it could not run
+    auto time_once = [&](size_t i) -> float {
+        if (flush && c->flush) launch_flush(c->flush, kFlushBytes, sink, st);
+        hipEventRecord(e0, st);
+        if (launch(cands[i], a, st) != hipSuccess) return -1.f;
+        hipEventRecord(e1, st);
+        float ms = 0.f;
+        if (hipEventSynchronize(e1) != hipSuccess || hipEventElapsedTime(&ms, e0, e1) != hipSuccess) return -1.f;
+        return ms * 1000.f;
+    };
+    auto median = [](std::vector<float> &t) {
+        std::sort(t.begin(), t.end());
+        return t[t.size() / 2];
+    };
+    // pass 1: every candidate, a few runs each
+    std::vector<std::pair<float, size_t>> ranked;
     for (size_t i = 0; i < cands.size(); ++i) {
         if (launch(cands[i], a, st) != hipSuccess) {  // warm-up; skip variants that cannot launch
             (void)hipGetLastError();
             continue;
         }
         std::vector<float> t;
-        bool ok = true;
-        for (int r = 0; r < reps && ok; ++r) {
-            if (flush && c->flush) launch_flush(c->flush, kFlushBytes, sink, st);
-            hipEventRecord(e0, st);
-            ok = launch(cands[i], a, st) == hipSuccess;
-            hipEventRecord(e1, st);
-            float ms = 0.f;
-            if (ok && hipEventSynchronize(e1) == hipSuccess && hipEventElapsedTime(&ms, e0, e1) == hipSuccess)
-                t.push_back(ms * 1000.f);
-            else
-                ok = false;
+        for (int r = 0; r < 7; ++r) {
+            const float us = time_once(i);
+            if (us < 0.f) break;
+            t.push_back(us);
         }
-        if (!ok || t.empty()) {
+        if (t.size() < 7) {
             (void)hipGetLastError();
             continue;
         }
-        std::sort(t.begin(), t.end());
-        const float med = t[t.size() / 2];
-        if (med < best) {
-            best = med;
-            best_i = static_cast<int>(i);
-        }
+        ranked.push_back({median(t), i});
     }
-    hipEventDestroy(e0);
-    hipEventDestroy(e1);
-    if (best_i < 0) {
+    if (ranked.empty()) {
+        hipEventDestroy(e0);
+        hipEventDestroy(e1);
         set_err(c, "no candidate could be launched");
         return PROJ_ERR_HIP;
+    }
+    // pass 2: the leaders again, interleaved round by round so that clock
+    // and thermal drift over the tuning run falls on all of them alike
+    std::sort(ranked.begin(), ranked.end());
+    const size_t lead = ranked.size() < 4 ? ranked.size() : 4;
+    std::vector<std::vector<float>> t2(lead);
+    for (int r = 0; r < 15; ++r)
+        for (size_t j = 0; j < lead; ++j) {
+            const float us = time_once(ranked[j].second);
+            if (us >= 0.f) t2[j].push_back(us);
+        }
+    (void)hipGetLastError();
+    hipEventDestroy(e0);
+    hipEventDestroy(e1);
+    float best = ranked[0].first;
+    size_t best_i = ranked[0].second;
+    bool first = true;
+    for (size_t j = 0; j < lead; ++j) {
+        if (t2[j].empty()) continue;
+        const float med = median(t2[j]);
+        if (first || med < best) {
+            best = med;
+            best_i = ranked[j].second;
+            first = false;
+        }
     }
     plan = Plan{cands[best_i], true, best};
     // leave the winner's result in Y

@@ -277,7 +277,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(Args a, int S) {
     X(4, 2, 8, 256, 3, 0) X(4, 4, 8, 256, 2, 0) X(4, 4, 4, 128, 4, 0) X(4, 4, 4, 128, 5, 0)                \
     X(4, 2, 4, 128, 4, 0) X(4, 2, 4, 128, 6, 0) X(4, 7, 4, 128, 3, 0)                                      \
     X(1, 2, 4, 128, 5, 1) X(1, 1, 8, 256, 4, 1) X(2, 4, 4, 128, 4, 1)                                      \
-    X(4, 7, 4, 128, 3, 1) X(4, 4, 4, 128, 4, 1) X(4, 2, 4, 128, 6, 1)
+    X(4, 7, 4, 128, 3, 1) X(4, 4, 4, 128, 4, 1) X(4, 2, 4, 128, 6, 1)                                      \
+    X(1, 2, 4, 128, 4, 1) X(1, 2, 4, 128, 6, 1) X(1, 2, 4, 128, 7, 1) X(1, 1, 4, 128, 6, 1)                \
+    X(1, 4, 4, 128, 4, 1) X(1, 2, 8, 256, 4, 1) X(1, 2, 8, 256, 3, 1) X(1, 1, 4, 128, 9, 1)
 
 #define PROJ_STREAM_INST(MT, NT, WV, KC, D, WNT)                                  \
     template __global__ void stream_kernel<MT, NT, WV, KC, D, WNT, false>(Args, int); \
