@@ -41,19 +41,17 @@ __device__ __forceinline__ float gelu_tanh(float v) {
     return v / (1.0f + __expf(-u2));
 }
 
-// The same GELU with a hardware reciprocal (about 1 ulp) in place of the
-// IEEE division: used on the large-M epilogues where the per-element cost
-// matters; the result differs from gelu_tanh by a few fp32 ulps.
+// The same GELU for the large-M epilogues, where the per-element cost
+// matters: the exponent -2u log2(e) = v (A + B v^2) with the constants
+// folded, the hardware base-2 exponential, and a hardware reciprocal (about
+// 1 ulp) in place of the IEEE division.  The result differs from gelu_tanh
+// by a few fp32 ulps; the limits (v for large v, -0 for very negative v) and
+// NaN propagation are the same.
 __device__ __forceinline__ float gelu_tanh_fast(float v) {
-    const float c2 = 2.0f * 0.7978845608028654f;
-    float u2 = c2 * (v + 0.044715f * v * v * v);
-    return v * __builtin_amdgcn_rcpf(1.0f + __expf(-u2));
-}
-
-__device__ __forceinline__ float apply_epilogue_fast(float acc, int epi, float bias) {
-    float v = acc + bias;  // bias is 0 when the epilogue has none
-    if (epi & 2) v = gelu_tanh_fast(v);
-    return v;
+    const float A = -2.0f * 0.7978845608028654f * 1.4426950408889634f;  // -2 sqrt(2/pi) log2(e)
+    const float B = A * 0.044715f;
+    const float z = v * __builtin_fmaf(v * v, B, A);
+    return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z));
 }
 
 // bias (fp32-widened bf16) is added to the finished fp32 sum, then GELU.

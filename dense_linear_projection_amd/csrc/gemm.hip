@@ -10,13 +10,15 @@
 // waiting"), and lay LDS out so a wave's fragment reads hit distinct banks
 // (same page, section "Shared memory has a layout problem too").
 //
-// Three kernel families, all candidates of the measured planner:
+// Four kernel families, all candidates of the measured planner:
 //   * gemm_kernel: WM x WN waves, 16x16x32 matrix ops, two LDS stages of
 //     BK = 64 (any tile from 128 x 128 up);
 //   * gemm_ring32_kernel: four waves of 128 x BN/2, 32x32x16 matrix ops, a
 //     five-slot LDS ring of BK = 32 stages, one barrier per stage;
 //   * gemm_pp_kernel: eight waves in two groups that alternate between a
-//     phase of matrix ops and a phase of LDS reads and DMA ("ping-pong").
+//     phase of matrix ops and a phase of LDS reads and DMA ("ping-pong");
+//   * gemm_pp64_kernel: the same with 128-byte LDS rows (k copied 64 at a
+//     time) in a ring of operand halves.
 // Both operands are K-major in memory (X[m, k], W[n, k]) and are staged the
 // same way: global -> LDS copies without a register round trip (one
 // instruction moves 64 lanes x 16 bytes), with 16-byte chunks XOR-swizzled by
@@ -165,6 +167,51 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(Args a) {
     }
 }
 
+// Column position of a value of tile row r in the bf16 LDS staging tile:
+// 32-column blocks are swapped when bit 0 of the row differs from bit 2.
+// Together with the pair exchange below, the 32-bit writes of one
+// instruction then cover each 64-byte run of a 128-byte bank window once.
+__device__ __forceinline__ int stage_col(int r, int c) { return c ^ ((((r >> 2) ^ r) & 1) << 5); }
+
+// two fp32 -> bf16 (round to nearest even) in one 32-bit word, lo first
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+    typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
+}
+
+// Write a wave's 32x32-layout accumulators (FM x FN blocks at tile rows
+// row0 + 32 i, columns col0 + 32 j), after bias and optional GELU, into the
+// bf16 staging tile t16[BM][BN] (columns placed by stage_col).  A lane holds
+// one column and pairs of adjacent rows; neighbouring lanes (columns c, c+1)
+// swap one value of each pair (DPP quad permutation 1,0,3,2), so that each
+// writes two adjacent columns of one row as one 32-bit word.
+template <int BN, int FM, int FN, bool GELU>
+__device__ __forceinline__ void stage_tile_bf16(uint16_t *t16, const f32x16 (&acc)[FM][FN], const float (&bias)[FN],
+                                                int row0, int col0, int lane) {
+    const int fr = lane & 31, fq = lane >> 5;
+    const bool odd = lane & 1;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const int col = col0 + j * 32 + (fr & ~1);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; v += 2) {
+                float e0 = acc[i][j][v] + bias[j], e1 = acc[i][j][v + 1] + bias[j];
+                if (GELU) {
+                    e0 = gelu_tanh_fast(e0);
+                    e1 = gelu_tanh_fast(e1);
+                }
+                const float send = odd ? e0 : e1;
+                const float recv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, true));
+                const float lo = odd ? recv : e0, hi = odd ? e1 : recv;
+                const int row = row0 + i * 32 + 8 * (v / 4) + (v % 4) + 4 * fq + (odd ? 1 : 0);
+                *reinterpret_cast<uint32_t *>(t16 + row * BN + stage_col(row, col)) = pack_bf16x2(lo, hi);
+            }
+    }
+}
+
 // Four-wave GEMM on a ring of BK = 32 stages in LDS, with 32x32x16 matrix
 // ops.  Each wave owns a 128 x (BN/2) sub-tile (4 x FN blocks of 32x32, all
 // 256 accumulator registers for BN = 256) and is the only wave on its SIMD,
@@ -196,10 +243,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(Args a) {
 // time between its matrix ops; a memory instruction issued right behind
 // another stalls the SIMD's matrix pipe, one issued between two matrix ops
 // is nearly free (measured: 1366 -> 1201 cycles per stage for BN = 256).
-// Epilogue: the tile is staged through LDS as bf16, 64-column halves XOR'd
-// by bit 2 of the row so that the two half-waves' rows (4 apart) write
-// different banks, then written with 16-byte row-contiguous stores; partial
-// tiles, fp32 output or an unaligned Y store element by element.
+// Epilogue: the tile is staged through LDS as bf16 (stage_tile_bf16: the
+// GELU choice is made once per tile, neighbouring lanes pair their values
+// into 32-bit writes), then written with 16-byte row-contiguous stores;
+// partial tiles, fp32 output or an unaligned Y store element by element.
 template <int BN, int GM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_ring32_kernel(Args a) {
     constexpr int BM = 256, BK = 32, D = 5, WN = 2, NW = 4;
@@ -397,28 +444,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         bias[j] = ((a.epi & 1) && n < N) ? bf16_bits_to_f32(a.bias[n]) : 0.f;
     }
     if (full) {
-        // bf16 tile [BM][BN] in LDS; a value of row r, column c sits at column
-        // c ^ (32 * ((r >> 2) & 1)).  Row bit 2 is this lane's fq for every
-        // value it holds, so the XOR is one per-lane constant.
+        // bf16 tile [BM][BN] in LDS, then 16-byte row-contiguous stores
         uint16_t *t16 = reinterpret_cast<uint16_t *>(lds);
-        uint16_t *lbase = t16 + (wm * TM + 4 * fq) * BN;
-        const int epi = a.epi;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            // the XOR applies to the whole column (j * 32 toggles bit 5)
-            uint16_t *cb = lbase + ((wn * TN + j * 32 + fr) ^ (fq << 5));
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    cb[(i * 32 + 8 * (v / 4) + (v % 4)) * BN] =
-                        f32_to_bf16_bits(apply_epilogue_fast(acc[i][j][v], epi, bias[j]));
-        }
+        if (a.epi & 2)
+            stage_tile_bf16<BN, FM, FN, true>(t16, acc, bias, wm * TM, wn * TN, lane);
+        else
+            stage_tile_bf16<BN, FM, FN, false>(t16, acc, bias, wm * TM, wn * TN, lane);
         __syncthreads();
         constexpr int CPR = BN / 8;  // 16-byte chunks per row
         for (int c = tid; c < BM * CPR; c += 256) {
             const int row = c / CPR, ch = c % CPR;
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(t16 + row * BN + ((ch * 8) ^ (((row >> 2) & 1) << 5)));
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(t16 + row * BN + stage_col(row, ch * 8));
             *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.Y) + (m0 + row) * N + n0 + ch * 8) = v;
         }
     } else {
@@ -556,12 +592,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     auto run = [&](auto grp_tag) {
         constexpr int GRP = decltype(grp_tag)::value;
         constexpr int NC = (TOTAL - 4 * GRP + NW - 1) / NW;
-        // prologue: stages 0..LEADK-1 by every wave, all landed and visible
+        // prologue: stages 0..LEADK-1 in flight, stage 0 landed and visible
+        // (the loop waits for stage t+1 while it works on stage t)
         for (int t = 0; t < LEADK; ++t) {
 #pragma unroll
             for (int j = 0; j < NC; ++j) copy(j, t, t);
         }
-        wait_vm<0>();
+        wait_vm<NC *(LEADK - 1)>();
         barrier_nofence();
         if (GRP == 1) barrier_nofence();
         bf16x8 af[FM][2], bfr[FN][2];
@@ -579,6 +616,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
             for (int j = 0; j < NC; ++j) copy(j, t + LEADK, cslot);
             if (GRP == 1) wait_vm<NC *(LEADK - 1)>();  // stage t+1 landed (this wave's part)
+            lds_wait_all();  // this wave's reads are done before the slot can be refilled
             barrier_nofence();
             // multiply phase
             lds_wait_all();
@@ -609,18 +647,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                       (reinterpret_cast<uintptr_t>(a.Y) % 16 == 0);
     if (full) {
         uint16_t *t16 = reinterpret_cast<uint16_t *>(lds);
-        uint16_t *lbase = t16 + (wm * TM + 4 * fq) * BN;
-        const int epi = a.epi;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            uint16_t *cb = lbase + ((wn * TN + j * 32 + fr) ^ (fq << 5));
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    cb[(i * 32 + 8 * (v / 4) + (v % 4)) * BN] =
-                        f32_to_bf16_bits(apply_epilogue_fast(acc[i][j][v], epi, bias[j]));
-        }
+        if (a.epi & 2)
+            stage_tile_bf16<BN, FM, FN, true>(t16, acc, bias, wm * TM, wn * TN, lane);
+        else
+            stage_tile_bf16<BN, FM, FN, false>(t16, acc, bias, wm * TM, wn * TN, lane);
         __syncthreads();
         // read-back: all of a thread's LDS reads first, then its stores
         constexpr int CPR = BN / 8;
@@ -630,7 +660,209 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int p = 0; p < NPASS; ++p) {
             const int c = tid + 512 * p, row = c / CPR, ch = c % CPR;
-            v[p] = *reinterpret_cast<const u32x4 *>(t16 + row * BN + ((ch * 8) ^ (((row >> 2) & 1) << 5)));
+            v[p] = *reinterpret_cast<const u32x4 *>(t16 + row * BN + stage_col(row, ch * 8));
+        }
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p) {
+            const int c = tid + 512 * p, row = c / CPR, ch = c % CPR;
+            *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.Y) + (m0 + row) * N + n0 + ch * 8) = v[p];
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int64_t n = n0 + wn * TN + j * 32 + fr;
+            if (n >= N) continue;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int64_t m = m0 + wm * TM + i * 32 + 8 * (v / 4) + 4 * fq + (v % 4);
+                    if (m < M) store_out(a.Y, a.out, m * N + n, apply_epilogue(acc[i][j][v], a.epi, bias[j]));
+                }
+        }
+    }
+}
+
+// Eight-wave ping-pong GEMM with 128-byte LDS rows.  The same two groups and
+// phases as gemm_pp_kernel, but each operand is copied 64 k-values at a time
+// (128 bytes per row), which halves the L2 requests of the 64-byte rows and
+// the address unit's stalls behind them.  A whole 256 x 256 x 64 stage would
+// leave room for only two stages in LDS, so the ring holds operand halves:
+// five 32 KB slots that take, in order, A(0), B(0), A(1), B(1), A(2), ...
+// (half h in slot h mod 5; A(T) / B(T) are the X / W rows of k-range
+// [64T, 64T + 64)).
+//   * k-step s (32 k-values) reads A(s/2), B(s/2) at byte offset 64 (s % 2)
+//     of each row; rows hold 16-byte chunks at position chunk ^ (row & 7);
+//   * group 0 reads step s in phase 2s and multiplies in 2s+1, group 1 is one
+//     phase behind; A(T), B(T) are last read in phase 4T+3;
+//   * in its read phase of step 2T each group copies its half of B(T+1), in
+//     that of step 2T+1 its half of A(T+2): the slots of A(T-1), B(T-1),
+//     free since phase 4T;
+//   * A(T+1) and B(T+1) must be in LDS before phase 4T+4: each wave waits for
+//     all but its copies of A(T+2) at the end of step 2T+1 (group 0 after
+//     its matrix ops, group 1 after its reads), just before the barrier that
+//     opens phase 4T+4; steps 2T have nothing to wait for.
+template <int BN, int GM>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_pp64_kernel(Args a) {
+    constexpr int BM = 256, NW = 8, SLOTS = 5, SLOT = 32 * 1024;
+    constexpr int TM = 64, TN = BN / 2;
+    constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr int ROWB = 128;
+    constexpr int A_BLK = BM / 8, B_BLK = BN / 8;      // 1 KB copies (8 rows of 128 bytes)
+    constexpr int NCA = A_BLK / NW, NCB = B_BLK / NW;  // copies per wave per half
+    static_assert(A_BLK % NW == 0 && B_BLK % NW == 0, "copies divide over the waves");
+    static_assert(BM * ROWB <= SLOT && BN * ROWB <= SLOT, "a half fits a slot");
+    static_assert(SLOTS * SLOT <= 160 * 1024 && BM * BN * 2 <= SLOTS * SLOT, "LDS budget");
+    static_assert(BN % 64 == 0, "epilogue swizzle works on 64-column halves");
+
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2, wg = wave & 3;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t M = a.M, N = a.N, K = a.K;
+
+    const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    const int64_t G = tiles_m * tiles_n;
+    int64_t L = blockIdx.x;
+    if (G % 8 == 0) L = (L % 8) * (G / 8) + L / 8;
+    const int64_t per_group = GM * tiles_n;
+    const int64_t group = L / per_group;
+    const int64_t first_m = group * GM;
+    const int64_t gsz = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
+    const int64_t tm = first_m + (L % per_group) % gsz;
+    const int64_t tn = (L % per_group) / gsz;
+    const int64_t m0 = tm * BM, n0 = tn * BN;
+
+    // copies: a group's half of an operand half is blocks
+    // grp * (BLK/2) + wg + 4 j; lane l of a copy fills row 8b + l/8,
+    // position l%8, which holds chunk (l%8) ^ (l/8)
+    const int drow = lane >> 3;
+    const int dchunk = (lane & 7) ^ drow;
+    const int64_t rows_a = (M - m0) < BM ? (M - m0) : BM;
+    const int64_t rows_b = (N - n0) < BN ? (N - n0) : BN;
+    const __amdgpu_buffer_rsrc_t rsrc_a = buffer_rsrc(a.X + m0 * K, static_cast<uint32_t>(rows_a * K * 2));
+    const __amdgpu_buffer_rsrc_t rsrc_b = buffer_rsrc(a.W + n0 * K, static_cast<uint32_t>(rows_b * K * 2));
+    const __amdgpu_buffer_rsrc_t rsrc_none = buffer_rsrc(a.X, 0);
+    const int KH = static_cast<int>(K / 64);  // k-ranges of 64
+    auto blk_a = [&](int j) { return grp * (A_BLK / 2) + wg + 4 * j; };
+    auto blk_b = [&](int j) { return grp * (B_BLK / 2) + wg + 4 * j; };
+    // this wave's copies of A(T) (into half-slot index 2T) or B(T) (2T+1)
+    auto copy_a = [&](int T) {
+        char *slot = lds + ((2 * T) % SLOTS) * SLOT;
+        const uint32_t soff = static_cast<uint32_t>((T < KH ? T : KH - 1) * ROWB);
+#pragma unroll
+        for (int j = 0; j < NCA; ++j) {
+            const int b = blk_a(j);
+            dma16_buf(T < KH ? rsrc_a : rsrc_none, static_cast<uint32_t>((b * 8 + drow) * K * 2 + dchunk * 16), soff,
+                      slot + b * 1024);
+        }
+    };
+    auto copy_b = [&](int T) {
+        char *slot = lds + ((2 * T + 1) % SLOTS) * SLOT;
+        const uint32_t soff = static_cast<uint32_t>((T < KH ? T : KH - 1) * ROWB);
+#pragma unroll
+        for (int j = 0; j < NCB; ++j) {
+            const int b = blk_b(j);
+            dma16_buf(T < KH ? rsrc_b : rsrc_none, static_cast<uint32_t>((b * 8 + drow) * K * 2 + dchunk * 16), soff,
+                      slot + b * 1024);
+        }
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    const int fr = lane & 31, fq = lane >> 5;
+    const int sw = fr & 7;
+    // fragment of 32 rows from row0 (a multiple of 32) of a half-slot, k-step
+    // parity p, k-half h: chunk 4p + 2h + l/32 of row row0 + l%32
+    auto frag = [&](const char *base, int row0, int p, int h) -> bf16x8 {
+        return *reinterpret_cast<const bf16x8 *>(base + (row0 + fr) * ROWB + (((4 * p + 2 * h + fq) ^ sw) << 4));
+    };
+
+    float bias[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const int64_t n = n0 + wn * TN + j * 32 + fr;
+        bias[j] = ((a.epi & 1) && n < N) ? bf16_bits_to_f32(a.bias[n]) : 0.f;
+    }
+
+    auto run = [&](auto grp_tag) {
+        constexpr int GRP = decltype(grp_tag)::value;
+        // prologue: A(0), B(0), A(1) in flight, A(0) and B(0) landed and visible
+        copy_a(0);
+        copy_b(0);
+        copy_a(1);
+        wait_vm<NCA>();
+        barrier_nofence();
+        if (GRP == 1) barrier_nofence();
+        bf16x8 af[FM][2], bfr[FN][2];
+        for (int T = 0; T < KH; ++T) {
+            const char *sa = lds + ((2 * T) % SLOTS) * SLOT, *sb = lds + ((2 * T + 1) % SLOTS) * SLOT;
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                // read phase of step 2T + p
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                    for (int i = 0; i < FM; ++i) af[i][h] = frag(sa, wm * TM + i * 32, p, h);
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) bfr[j][h] = frag(sb, wn * TN + j * 32, p, h);
+                }
+                if (p == 0)
+                    copy_b(T + 1);
+                else
+                    copy_a(T + 2);
+                if (GRP == 1 && p == 1) wait_vm<NCA>();  // A(T+1), B(T+1) landed (this wave's part)
+                lds_wait_all();  // this wave's reads are done before the slot can be refilled
+                barrier_nofence();
+                // multiply phase
+                lds_wait_all();
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int i = 0; i < FM; ++i)
+#pragma unroll
+                        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16(af[i][h], bfr[j][h], acc[i][j]);
+                if (GRP == 0 && p == 1) wait_vm<NCA>();
+                barrier_nofence();
+            }
+        }
+        if (GRP == 0) barrier_nofence();
+    };
+    if (KH > 0) {
+        if (grp == 0)
+            run(std::integral_constant<int, 0>{});
+        else
+            run(std::integral_constant<int, 1>{});
+    }
+    // copies past the end (empty resource) still write LDS: drain them
+    wait_vm<0>();
+    __syncthreads();
+
+    const bool full = (m0 + BM <= M) && (n0 + BN <= N) && (N % 8 == 0) && a.out == OUT_BF16 &&
+                      (reinterpret_cast<uintptr_t>(a.Y) % 16 == 0);
+    if (full) {
+        uint16_t *t16 = reinterpret_cast<uint16_t *>(lds);
+        if (a.epi & 2)
+            stage_tile_bf16<BN, FM, FN, true>(t16, acc, bias, wm * TM, wn * TN, lane);
+        else
+            stage_tile_bf16<BN, FM, FN, false>(t16, acc, bias, wm * TM, wn * TN, lane);
+        __syncthreads();
+        constexpr int CPR = BN / 8;
+        constexpr int NPASS = BM * CPR / 512;
+        static_assert(BM * CPR % 512 == 0, "whole passes");
+        u32x4 v[NPASS];
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p) {
+            const int c = tid + 512 * p, row = c / CPR, ch = c % CPR;
+            v[p] = *reinterpret_cast<const u32x4 *>(t16 + row * BN + stage_col(row, ch * 8));
         }
 #pragma unroll
         for (int p = 0; p < NPASS; ++p) {
@@ -670,6 +902,10 @@ PROJ_GEMM_RING32_VARIANTS(PROJ_GEMM_RING32_INST)
 #define PROJ_GEMM_PP_VARIANTS(X) X(256, 4) X(256, 8) X(192, 4)
 #define PROJ_GEMM_PP_INST(BN, GM) template __global__ void gemm_pp_kernel<BN, GM>(Args);
 PROJ_GEMM_PP_VARIANTS(PROJ_GEMM_PP_INST)
+
+#define PROJ_GEMM_PP64_VARIANTS(X) X(256, 4) X(256, 8) X(192, 4)
+#define PROJ_GEMM_PP64_INST(BN, GM) template __global__ void gemm_pp64_kernel<BN, GM>(Args);
+PROJ_GEMM_PP64_VARIANTS(PROJ_GEMM_PP64_INST)
 
 #ifndef __HIP_DEVICE_COMPILE__
 template <int BM, int BN, int BK, int WM, int WN, int GM>
@@ -728,14 +964,32 @@ static hipError_t launch_gemm_pp(const Args &a, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <int BN, int GM>
+static hipError_t prepare_gemm_pp64() {
+    auto fn = gemm_pp64_kernel<BN, GM>;
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               5 * 32 * 1024);
+}
+
+template <int BN, int GM>
+static hipError_t launch_gemm_pp64(const Args &a, hipStream_t st) {
+    const int64_t G = ((a.M + 255) / 256) * ((a.N + BN - 1) / BN);
+    if (G <= 0 || G > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((gemm_pp64_kernel<BN, GM>), dim3(static_cast<unsigned>(G)), dim3(512), 5 * 32 * 1024, st, a);
+    return hipGetLastError();
+}
+
 #define PROJ_GEMM_ENTRY(BM, BN, WM, WN, GM) \
     {"gemm", BM, BN, 64, 64, WM, WN, GM, 0, &launch_gemm<BM, BN, 64, WM, WN, GM>, &prepare_gemm<BM, BN, 64, WM, WN, GM>},
 #define PROJ_GEMM_RING32_ENTRY(BN, GM) \
     {"gemmring32", 256, BN, 32, 64, 2, 2, GM, kRingMaxK, &launch_gemm_ring32<BN, GM>, &prepare_gemm_ring32<BN, GM>},
 #define PROJ_GEMM_PP_ENTRY(BN, GM) \
     {"gemmpp", 256, BN, 32, 32, 4, 2, GM, kRingMaxK, &launch_gemm_pp<BN, GM>, &prepare_gemm_pp<BN, GM>},
+#define PROJ_GEMM_PP64_ENTRY(BN, GM) \
+    {"gemmpp64", 256, BN, 64, 64, 4, 2, GM, kRingMaxK, &launch_gemm_pp64<BN, GM>, &prepare_gemm_pp64<BN, GM>},
 const GemmVariant kGemmVariants[] = {PROJ_GEMM_VARIANTS(PROJ_GEMM_ENTRY) PROJ_GEMM_RING32_VARIANTS(PROJ_GEMM_RING32_ENTRY)
-                                         PROJ_GEMM_PP_VARIANTS(PROJ_GEMM_PP_ENTRY)};
+                                         PROJ_GEMM_PP_VARIANTS(PROJ_GEMM_PP_ENTRY)
+                                             PROJ_GEMM_PP64_VARIANTS(PROJ_GEMM_PP64_ENTRY)};
 const int kNumGemmVariants = sizeof(kGemmVariants) / sizeof(kGemmVariants[0]);
 #endif
 

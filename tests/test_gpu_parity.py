@@ -43,6 +43,7 @@ INT_SHAPES = [
     (1, 48, 4104),     # one token row, K % 32 == 8, many k-steps
     (300, 520, 512),   # large-M family, ragged M and N
     (257, 129, 128),
+    (300, 256, 64),    # large-M family, a single 64-wide k-range
 ]
 
 
