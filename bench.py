@@ -42,7 +42,7 @@ LLC_BYTES = 256 << 20          # last-level (Infinity) cache
 FAMILY_SOURCES = {
     "stream_kernel": ["stream.hip", "common.hpp"],
     "gemm_pp_kernel": ["gemm.hip", "common.hpp"],
-    "gemm_ring32_kernel": ["gemm.hip", "common.hpp"],
+    "gemm_pp64_kernel": ["gemm.hip", "common.hpp"],
     "gemm_kernel": ["gemm.hip", "common.hpp"],
 }
 

@@ -10,15 +10,14 @@
 // waiting"), and lay LDS out so a wave's fragment reads hit distinct banks
 // (same page, section "Shared memory has a layout problem too").
 //
-// Four kernel families, all candidates of the measured planner:
+// Three kernel families, all candidates of the measured planner:
 //   * gemm_kernel: WM x WN waves, 16x16x32 matrix ops, two LDS stages of
 //     BK = 64 (any tile from 128 x 128 up);
-//   * gemm_ring32_kernel: four waves of 128 x BN/2, 32x32x16 matrix ops, a
-//     five-slot LDS ring of BK = 32 stages, one barrier per stage;
 //   * gemm_pp_kernel: eight waves in two groups that alternate between a
-//     phase of matrix ops and a phase of LDS reads and DMA ("ping-pong");
+//     phase of matrix ops and a phase of LDS reads and DMA ("ping-pong"),
+//     32x32x16 matrix ops on 64-byte LDS rows (K a multiple of 32);
 //   * gemm_pp64_kernel: the same with 128-byte LDS rows (k copied 64 at a
-//     time) in a ring of operand halves.
+//     time) in a ring of operand halves (K a multiple of 64).
 // Both operands are K-major in memory (X[m, k], W[n, k]) and are staged the
 // same way: global -> LDS copies without a register round trip (one
 // instruction moves 64 lanes x 16 bytes), with 16-byte chunks XOR-swizzled by
@@ -212,267 +211,6 @@ __device__ __forceinline__ void stage_tile_bf16(uint16_t *t16, const f32x16 (&ac
     }
 }
 
-// Four-wave GEMM on a ring of BK = 32 stages in LDS, with 32x32x16 matrix
-// ops.  Each wave owns a 128 x (BN/2) sub-tile (4 x FN blocks of 32x32, all
-// 256 accumulator registers for BN = 256) and is the only wave on its SIMD,
-// so it hides its own latencies:
-//   * a stage (256 rows of X and BN rows of W, 32 k each) is two k-halves;
-//     group g = 4h + i runs the FN matrix ops of A block i, k-half h;
-//   * the A fragment of group g is read two groups ahead (the last two
-//     groups read the next stage's first two); k-half 1 B fragments of the
-//     current stage are read in groups 0..3, k-half 0 B fragments of the next
-//     stage in groups 4..7, so a stage starts with its first operands in
-//     registers;
-//   * one barrier per stage, before group 4: each wave first waits for its
-//     own DMA copies of stage t+1, the barrier then makes stage t+1 visible
-//     to all waves and proves that the slot of stage t-1 is no longer read;
-//   * D = 5 slots and one DMA copy per group: the first half of the copies
-//     of stage t+4 in the second half of stage t (into the slot of stage
-//     t-1), the rest of stage t+3 in the first half of stage t, so a slot is
-//     refilled three stages before it is read and the address unit sees an
-//     even load;
-//   * rows of 64 bytes hold 16-byte chunks at position chunk ^ ((row >> 2) & 3).
-//     For the 32x32 fragment read (lanes 0..31 one chunk of 32 rows, lanes
-//     32..63 the next chunk of the same rows) this is the swizzle with no
-//     LDS bank conflicts: measured with SQ_LDS_BANK_CONFLICT on each
-//     candidate pattern, (row >> 1) & 3 costs 4 conflict cycles per read here
-//     (it is the conflict-free one for 16-row fragments) and no swizzle 12.
-//     The DMA writes lane i to position i, so the XOR picks each lane's
-//     source.
-// Scheduling-group barriers place each group's memory instructions one at a
-// time between its matrix ops; a memory instruction issued right behind
-// another stalls the SIMD's matrix pipe, one issued between two matrix ops
-// is nearly free (measured: 1366 -> 1201 cycles per stage for BN = 256).
-// Epilogue: the tile is staged through LDS as bf16 (stage_tile_bf16: the
-// GELU choice is made once per tile, neighbouring lanes pair their values
-// into 32-bit writes), then written with 16-byte row-contiguous stores;
-// partial tiles, fp32 output or an unaligned Y store element by element.
-template <int BN, int GM>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_ring32_kernel(Args a) {
-    constexpr int BM = 256, BK = 32, D = 5, WN = 2, NW = 4;
-    constexpr int TM = 128, TN = BN / 2;
-    constexpr int FM = TM / 32, FN = TN / 32;
-    constexpr int NG = 2 * FM;                       // groups per stage
-    constexpr int MID = NG / 2;                      // group before which the barrier sits
-    constexpr int ROWB = BK * 2;                     // 64 bytes per row per stage
-    constexpr int STAGE = (BM + BN) * ROWB;
-    constexpr int A_BLK = BM / 16, B_BLK = BN / 16;  // 1 KB DMA blocks (16 rows)
-    constexpr int PERW = (A_BLK + B_BLK) / NW;       // DMA copies per wave per stage
-    constexpr int PA = A_BLK / NW;
-    constexpr int NBG = (FN + MID - 1) / MID;        // B fragments read per group
-    constexpr int PH = (PERW + 1) / 2;                // copies of stage t+4 issued in stage t
-    constexpr int NC1 = (PH + MID - 1) / MID;         // per group, second half
-    constexpr int NC2 = (PERW - PH + MID - 1) / MID;  // per group, first half
-    constexpr int LEAD = 2 * PERW;                    // copies still in flight at the barrier
-    static_assert(A_BLK % NW == 0 && B_BLK % NW == 0, "copies divide over the waves");
-    static_assert(1 + NBG <= 15, "lgkmcnt range");
-    static_assert(D * STAGE <= 160 * 1024 && BM * BN * 2 <= D * STAGE, "LDS budget");
-    static_assert(LEAD + PH <= 63, "vmcnt range");
-    static_assert(BN % 64 == 0, "epilogue swizzle works on 64-column halves");
-    static_assert(FN >= 3 && NBG == 1 && NC1 <= 1 && NC2 <= 1, "interleave: <= 2 reads and 1 copy per group");
-
-    extern __shared__ __attribute__((aligned(16))) char lds[];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / WN, wn = wave % WN;
-    const int64_t M = a.M, N = a.N, K = a.K;
-
-    const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    const int64_t G = tiles_m * tiles_n;
-    int64_t L = blockIdx.x;
-    if (G % 8 == 0) L = (L % 8) * (G / 8) + L / 8;
-    const int64_t per_group = GM * tiles_n;
-    const int64_t group = L / per_group;
-    const int64_t first_m = group * GM;
-    const int64_t gsz = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
-    const int64_t tm = first_m + (L % per_group) % gsz;
-    const int64_t tn = (L % per_group) / gsz;
-    const int64_t m0 = tm * BM, n0 = tn * BN;
-
-    // DMA: block b (16 rows) of a stage is one 1 KB copy; lane l fills row
-    // 16b + l/4, position l%4, which holds chunk (l%4) ^ ((l/16)%4).  The
-    // first A_BLK/NW copies of each wave are X blocks, the rest W blocks.
-    // Each operand is read through a buffer resource over the tile's valid
-    // rows: rows past M or N read as zero, the per-lane offset is fixed for
-    // the whole loop and the k offset is a scalar.
-    const int drow = lane >> 2;
-    const int dchunk = (lane & 3) ^ ((lane >> 4) & 3);
-    const int64_t rows_a = (M - m0) < BM ? (M - m0) : BM;
-    const int64_t rows_b = (N - n0) < BN ? (N - n0) : BN;
-    const __amdgpu_buffer_rsrc_t rsrc_a = buffer_rsrc(a.X + m0 * K, static_cast<uint32_t>(rows_a * K * 2));
-    const __amdgpu_buffer_rsrc_t rsrc_b = buffer_rsrc(a.W + n0 * K, static_cast<uint32_t>(rows_b * K * 2));
-    uint32_t voff[PERW];
-#pragma unroll
-    for (int j = 0; j < PERW; ++j) {
-        const int r = (j < PA ? (wave + j * NW) : (wave + (j - PA) * NW)) * 16 + drow;
-        voff[j] = static_cast<uint32_t>(r * K * 2 + dchunk * 16);
-    }
-    const int KT = static_cast<int>(K / BK);  // K < 2^22 (planner limit)
-    // stages past the end go through an empty resource: no memory traffic,
-    // but the copy still counts for the vmcnt waits
-    const __amdgpu_buffer_rsrc_t rsrc_none = buffer_rsrc(a.X, 0);
-    // copy j of stage t into ring slot `slot` (= t % D, kept by the caller)
-    auto copy = [&](int j, int t, int slot) {
-        const uint32_t soff = static_cast<uint32_t>((t < KT ? t : KT - 1) * (BK * 2));
-        const int blk = j < PA ? wave + j * NW : A_BLK + wave + (j - PA) * NW;
-        dma16_buf(t < KT ? (j < PA ? rsrc_a : rsrc_b) : rsrc_none, voff[j], soff, lds + slot * STAGE + blk * 1024);
-    };
-    // slot of stage t + d given the slot of stage t
-    auto slot_add = [](int slot, int d) { return slot + d >= D ? slot + d - D : slot + d; };
-
-    f32x16 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-    // fragment of 32 rows starting at row0 (a multiple of 32), k-half h:
-    // lane l reads row row0 + l%32, chunk 2h + l/32
-    const int fr = lane & 31, fq = lane >> 5;
-    const int sw = (fr >> 2) & 3;
-    auto frag = [&](const char *base, int row0, int h) -> bf16x8 {
-        return *reinterpret_cast<const bf16x8 *>(base + (row0 + fr) * ROWB + (((2 * h + fq) ^ sw) << 4));
-    };
-
-
-    if (KT > 0) {
-        // stages 0..2 and the first part of stage 3 in flight; stage 0
-        // landed and visible
-#pragma unroll
-        for (int j = 0; j < PERW; ++j) copy(j, 0, 0);
-#pragma unroll
-        for (int j = 0; j < PERW; ++j) copy(j, 1, 1);
-#pragma unroll
-        for (int j = 0; j < PERW; ++j) copy(j, 2, 2);
-#pragma unroll
-        for (int j = 0; j < PH; ++j) copy(j, 3, 3);
-        wait_vm<2 * PERW + PH>();
-        __syncthreads();
-    }
-
-    // b0x: k-half 0 fragments of the current stage (x alternates between
-    // stages), b1: k-half 1 of the current stage, a0x: A fragments by group
-    // (entries NG, NG+1 are the next stage's groups 0 and 1)
-    bf16x8 b0e[FN], b0o[FN], b1[FN], a0e[NG + 2], a0o[NG + 2];
-    {
-        const char *sa = lds, *sb = sa + BM * ROWB;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) b0e[j] = frag(sb, wn * TN + j * 32, 0);
-        a0e[0] = frag(sa, wm * TM, 0);
-        a0e[1] = frag(sa, wm * TM + 32, 0);
-        lds_wait_all();
-    }
-
-    auto stage = [&](int kt, int slot, bf16x8(&bc)[FN], bf16x8(&bn)[FN], bf16x8(&ac)[NG + 2],
-                     bf16x8(&an)[NG + 2]) {
-        const char *sa = lds + slot * STAGE, *sb = sa + BM * ROWB;
-        const char *na = lds + slot_add(slot, 1) * STAGE, *nb = na + BM * ROWB;
-        const int slot3 = slot_add(slot, 3), slot_last = slot_add(slot, D - 1);
-#pragma unroll
-        for (int g = 0; g < NG; ++g) {
-            const int h = g / FM, i = g % FM;
-            if (g == MID) {
-                // stage kt+1 landed for this wave, then for all waves; the
-                // slot of stage kt-1 is no longer read
-                wait_vm<LEAD>();
-                lds_wait_all();
-                __builtin_amdgcn_s_barrier();
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            // every LDS read but the previous group's has landed
-            if (g == MID)
-                lds_wait_keep<0>();
-            else
-                lds_wait_keep<1 + NBG>();
-            const int gn = g + 2;
-            if (gn < NG)
-                ac[gn] = frag(sa, wm * TM + (gn % FM) * 32, gn / FM);
-            else
-                an[gn - NG] = frag(na, wm * TM + (gn - NG) * 32, 0);
-            const int q0 = (g % MID) * NBG;
-#pragma unroll
-            for (int q = q0; q < q0 + NBG && q < FN; ++q) {
-                if (g < MID)
-                    b1[q] = frag(sb, wn * TN + q * 32, 1);
-                else
-                    bn[q] = frag(nb, wn * TN + q * 32, 0);
-            }
-            if (g >= MID) {
-                const int c0 = (g - MID) * NC1;
-#pragma unroll
-                for (int c = c0; c < c0 + NC1 && c < PH; ++c) copy(c, kt + D - 1, slot_last);
-            } else {
-                const int c0 = PH + g * NC2;
-#pragma unroll
-                for (int c = c0; c < c0 + NC2 && c < PERW; ++c) copy(c, kt + 3, slot3);
-            }
-#pragma unroll
-            for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16(ac[g], h == 0 ? bc[j] : b1[j], acc[i][j]);
-            // one memory instruction between two matrix ops: A read, B read,
-            // copy, each issued while the matrix pipe is busy (issued back to
-            // back they stall it)
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, FN - 3, 0);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    };
-    // KT is even: the planner offers this kernel only for K % 64 == 0
-    for (int kt = 0, slot = 0; kt < KT; kt += 2) {
-        stage(kt, slot, b0e, b0o, a0e, a0o);
-        slot = slot_add(slot, 1);
-        stage(kt + 1, slot, b0o, b0e, a0o, a0e);
-        slot = slot_add(slot, 1);
-    }
-    wait_vm<0>();
-    lds_wait_all();
-    __syncthreads();
-
-    // ---- epilogue
-    const bool full = (m0 + BM <= M) && (n0 + BN <= N) && (N % 8 == 0) && a.out == OUT_BF16 &&
-                      (reinterpret_cast<uintptr_t>(a.Y) % 16 == 0);
-    float bias[FN];
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-        const int64_t n = n0 + wn * TN + j * 32 + fr;
-        bias[j] = ((a.epi & 1) && n < N) ? bf16_bits_to_f32(a.bias[n]) : 0.f;
-    }
-    if (full) {
-        // bf16 tile [BM][BN] in LDS, then 16-byte row-contiguous stores
-        uint16_t *t16 = reinterpret_cast<uint16_t *>(lds);
-        if (a.epi & 2)
-            stage_tile_bf16<BN, FM, FN, true>(t16, acc, bias, wm * TM, wn * TN, lane);
-        else
-            stage_tile_bf16<BN, FM, FN, false>(t16, acc, bias, wm * TM, wn * TN, lane);
-        __syncthreads();
-        constexpr int CPR = BN / 8;  // 16-byte chunks per row
-        for (int c = tid; c < BM * CPR; c += 256) {
-            const int row = c / CPR, ch = c % CPR;
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(t16 + row * BN + stage_col(row, ch * 8));
-            *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.Y) + (m0 + row) * N + n0 + ch * 8) = v;
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int64_t n = n0 + wn * TN + j * 32 + fr;
-            if (n >= N) continue;
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int64_t m = m0 + wm * TM + i * 32 + 8 * (v / 4) + 4 * fq + (v % 4);
-                    if (m < M) store_out(a.Y, a.out, m * N + n, apply_epilogue(acc[i][j][v], a.epi, bias[j]));
-                }
-        }
-    }
-}
-
 // Barrier without a memory fence (the waits are explicit): the empty asm
 // statements keep the compiler from moving memory accesses across it, the
 // scheduling fences keep every other instruction on its side.
@@ -494,9 +232,16 @@ __device__ __forceinline__ void barrier_nofence() {
 // other wave's memory instructions issue, instead of one wave interleaving
 // both.
 //   * tile 256 x BN, BK = 32 stages in a D = 5 slot LDS ring (64-byte rows,
-//     16-byte chunks at position chunk ^ ((row >> 2) & 3), as in the ring
-//     kernels); wave w owns rows 64 (w / 2) .. +63 and columns
-//     (BN / 2) (w % 2) .. +BN/2-1: 2 x FN blocks of 32 x 32;
+//     16-byte chunks at position chunk ^ ((row >> 2) & 3)); wave w owns rows
+//     64 (w / 2) .. +63 and columns (BN / 2) (w % 2) .. +BN/2-1: 2 x FN
+//     blocks of 32 x 32;
+//   * the swizzle: a 32x32 fragment read takes one chunk of 32 rows in
+//     lanes 0..31 and the next chunk of the same rows in lanes 32..63.
+//     Measured with SQ_LDS_BANK_CONFLICT over the candidate patterns,
+//     (row >> 2) & 3 has no bank conflicts here, (row >> 1) & 3 (the
+//     conflict-free one for 16-row fragments) costs 4 conflict cycles per
+//     read and no swizzle 12.  The DMA writes lane i to position i, so the
+//     XOR picks each lane's source;
 //   * group 0 reads stage t in phase 2t and multiplies in phase 2t+1;
 //   * group 1 is one phase behind: reads in 2t+1, multiplies in 2t+2;
 //   * in its read phase for stage t each group issues its copies of stage
@@ -615,8 +360,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const int cslot = slot_add(slot, LEADK);
 #pragma unroll
             for (int j = 0; j < NC; ++j) copy(j, t + LEADK, cslot);
-            if (GRP == 1) wait_vm<NC *(LEADK - 1)>();  // stage t+1 landed (this wave's part)
-            lds_wait_all();  // this wave's reads are done before the slot can be refilled
+            if (GRP == 1) {
+                wait_vm<NC *(LEADK - 1)>();  // stage t+1 landed (this wave's part)
+                // the next phase is group 0's read phase of stage t+1, which
+                // refills the slot of stage t: this wave's reads of stage t,
+                // the last of that slot, must have landed
+                lds_wait_all();
+            }
             barrier_nofence();
             // multiply phase
             lds_wait_all();
@@ -642,7 +392,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     wait_vm<0>();
     __syncthreads();
 
-    // ---- epilogue (LDS staging as in the 32x32 ring kernel)
+    // ---- epilogue: the tile is staged through LDS as bf16 (stage_tile_bf16),
+    // then written with 16-byte row-contiguous stores; partial tiles, fp32
+    // output or an unaligned Y store element by element
     const bool full = (m0 + BM <= M) && (n0 + BN <= N) && (N % 8 == 0) && a.out == OUT_BF16 &&
                       (reinterpret_cast<uintptr_t>(a.Y) % 16 == 0);
     if (full) {
@@ -818,8 +570,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     copy_b(T + 1);
                 else
                     copy_a(T + 2);
-                if (GRP == 1 && p == 1) wait_vm<NCA>();  // A(T+1), B(T+1) landed (this wave's part)
-                lds_wait_all();  // this wave's reads are done before the slot can be refilled
+                if (GRP == 1 && p == 1) {
+                    wait_vm<NCA>();  // A(T+1), B(T+1) landed (this wave's part)
+                    // the next phase is group 0's read phase of step 2T+2,
+                    // which refills the slot of A(T): this wave's reads of
+                    // step 2T+1, the last of A(T), must have landed
+                    lds_wait_all();
+                }
                 barrier_nofence();
                 // multiply phase
                 lds_wait_all();
@@ -895,9 +652,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #define PROJ_GEMM_INST(BM, BN, WM, WN, GM) template __global__ void gemm_kernel<BM, BN, 64, WM, WN, GM>(Args);
 PROJ_GEMM_VARIANTS(PROJ_GEMM_INST)
 
-#define PROJ_GEMM_RING32_VARIANTS(X) X(256, 4) X(192, 4)
-#define PROJ_GEMM_RING32_INST(BN, GM) template __global__ void gemm_ring32_kernel<BN, GM>(Args);
-PROJ_GEMM_RING32_VARIANTS(PROJ_GEMM_RING32_INST)
 
 #define PROJ_GEMM_PP_VARIANTS(X) X(256, 4) X(256, 8) X(192, 4)
 #define PROJ_GEMM_PP_INST(BN, GM) template __global__ void gemm_pp_kernel<BN, GM>(Args);
@@ -928,25 +682,9 @@ static hipError_t launch_gemm(const Args &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-// The ring and ping-pong kernels address a 256-row tile through 32-bit
-// buffer offsets.
+// The ping-pong kernels address a 256-row tile through 32-bit buffer
+// offsets.
 constexpr int64_t kRingMaxK = (int64_t{1} << 31) / (256 * 2);
-
-template <int BN, int GM>
-static hipError_t prepare_gemm_ring32() {
-    auto fn = gemm_ring32_kernel<BN, GM>;
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
-                               5 * (256 + BN) * 64);
-}
-
-template <int BN, int GM>
-static hipError_t launch_gemm_ring32(const Args &a, hipStream_t st) {
-    const int64_t G = ((a.M + 255) / 256) * ((a.N + BN - 1) / BN);
-    if (G <= 0 || G > 0x7fffffff) return hipErrorInvalidConfiguration;
-    constexpr int lds_bytes = 5 * (256 + BN) * 64;
-    hipLaunchKernelGGL((gemm_ring32_kernel<BN, GM>), dim3(static_cast<unsigned>(G)), dim3(256), lds_bytes, st, a);
-    return hipGetLastError();
-}
 
 template <int BN, int GM>
 static hipError_t prepare_gemm_pp() {
@@ -981,15 +719,12 @@ static hipError_t launch_gemm_pp64(const Args &a, hipStream_t st) {
 
 #define PROJ_GEMM_ENTRY(BM, BN, WM, WN, GM) \
     {"gemm", BM, BN, 64, 64, WM, WN, GM, 0, &launch_gemm<BM, BN, 64, WM, WN, GM>, &prepare_gemm<BM, BN, 64, WM, WN, GM>},
-#define PROJ_GEMM_RING32_ENTRY(BN, GM) \
-    {"gemmring32", 256, BN, 32, 64, 2, 2, GM, kRingMaxK, &launch_gemm_ring32<BN, GM>, &prepare_gemm_ring32<BN, GM>},
 #define PROJ_GEMM_PP_ENTRY(BN, GM) \
     {"gemmpp", 256, BN, 32, 32, 4, 2, GM, kRingMaxK, &launch_gemm_pp<BN, GM>, &prepare_gemm_pp<BN, GM>},
 #define PROJ_GEMM_PP64_ENTRY(BN, GM) \
     {"gemmpp64", 256, BN, 64, 64, 4, 2, GM, kRingMaxK, &launch_gemm_pp64<BN, GM>, &prepare_gemm_pp64<BN, GM>},
-const GemmVariant kGemmVariants[] = {PROJ_GEMM_VARIANTS(PROJ_GEMM_ENTRY) PROJ_GEMM_RING32_VARIANTS(PROJ_GEMM_RING32_ENTRY)
-                                         PROJ_GEMM_PP_VARIANTS(PROJ_GEMM_PP_ENTRY)
-                                             PROJ_GEMM_PP64_VARIANTS(PROJ_GEMM_PP64_ENTRY)};
+const GemmVariant kGemmVariants[] = {PROJ_GEMM_VARIANTS(PROJ_GEMM_ENTRY) PROJ_GEMM_PP_VARIANTS(PROJ_GEMM_PP_ENTRY)
+                                         PROJ_GEMM_PP64_VARIANTS(PROJ_GEMM_PP64_ENTRY)};
 const int kNumGemmVariants = sizeof(kGemmVariants) / sizeof(kGemmVariants[0]);
 #endif
 
