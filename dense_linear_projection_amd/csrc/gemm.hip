@@ -10,14 +10,16 @@
 // waiting"), and lay LDS out so a wave's fragment reads hit distinct banks
 // (same page, section "Shared memory has a layout problem too").
 //
-// Three kernel families, all candidates of the measured planner:
+// Four kernel families, all candidates of the measured planner:
 //   * gemm_kernel: WM x WN waves, 16x16x32 matrix ops, two LDS stages of
 //     BK = 64 (any tile from 128 x 128 up);
 //   * gemm_pp_kernel: eight waves in two groups that alternate between a
 //     phase of matrix ops and a phase of LDS reads and DMA ("ping-pong"),
 //     32x32x16 matrix ops on 64-byte LDS rows (K a multiple of 32);
 //   * gemm_pp64_kernel: the same with 128-byte LDS rows (k copied 64 at a
-//     time) in a ring of operand halves (K a multiple of 64).
+//     time) in a ring of operand halves (K a multiple of 64);
+//   * gemm_pp64p_kernel: its persistent form, one workgroup per CU walking
+//     tiles with the ring running on across them.
 // Both operands are K-major in memory (X[m, k], W[n, k]) and are staged the
 // same way: global -> LDS copies without a register round trip (one
 // instruction moves 64 lanes x 16 bytes), with 16-byte chunks XOR-swizzled by
@@ -642,6 +644,238 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 }
 
+// Persistent form of gemm_pp64_kernel: one workgroup per CU walks tiles
+// blockIdx.x, blockIdx.x + gridDim.x, ...  The LDS ring runs on across tiles
+// (the copies the last k-ranges of a tile would make past K fetch the next
+// tile's A(0), B(0), A(1) instead), so the next tile's first operands are in
+// flight while this tile finishes and its epilogue runs, and there is no
+// workgroup launch between tiles.  The epilogue stages the tile through the
+// two slots the last k-range frees (the other three hold the next tile's
+// first halves): group 0's rows 0..127 first, then group 1's rows 128..255,
+// each 64-row wave block in one slot.  Needs K >= 128 (two k-ranges), so
+// that the ring's look-ahead stays within the next tile.
+template <int BN, int GM>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_pp64p_kernel(Args a) {
+    constexpr int BM = 256, NW = 8, SLOTS = 5, SLOT = 32 * 1024;
+    constexpr int TM = 64, TN = BN / 2;
+    constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr int ROWB = 128;
+    constexpr int A_BLK = BM / 8, B_BLK = BN / 8;
+    constexpr int NCA = A_BLK / NW, NCB = B_BLK / NW;
+    static_assert(A_BLK % NW == 0 && B_BLK % NW == 0, "copies divide over the waves");
+    static_assert(BM * ROWB <= SLOT && BN * ROWB <= SLOT && TM * BN * 2 <= SLOT, "halves and staging fit a slot");
+    static_assert(SLOTS * SLOT <= 160 * 1024, "LDS budget");
+    static_assert(BN % 64 == 0, "epilogue swizzle works on 64-column halves");
+
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2, wg = wave & 3;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t M = a.M, N = a.N, K = a.K;
+    const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    const int64_t G = tiles_m * tiles_n;
+    const int KH = static_cast<int>(K / 64);
+
+    // tile -> origin: XCD-contiguous renumbering (a workgroup's tiles all
+    // lie on its XCD, since gridDim.x is a multiple of 8), then GM-row groups
+    auto origin = [&](int64_t tile, int64_t &m0, int64_t &n0) {
+        int64_t L = tile;
+        if (G % 8 == 0) L = (L % 8) * (G / 8) + L / 8;
+        const int64_t per_group = GM * tiles_n;
+        const int64_t first_m = (L / per_group) * GM;
+        const int64_t gsz = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
+        m0 = (first_m + (L % per_group) % gsz) * BM;
+        n0 = ((L % per_group) / gsz) * BN;
+    };
+    // buffer resources over a tile's valid X and W rows (empty past the last tile)
+    auto resources = [&](int64_t tile, __amdgpu_buffer_rsrc_t &ra, __amdgpu_buffer_rsrc_t &rb) {
+        if (tile >= G) {
+            ra = rb = buffer_rsrc(a.X, 0);
+            return;
+        }
+        int64_t m0, n0;
+        origin(tile, m0, n0);
+        const int64_t rows_a = (M - m0) < BM ? (M - m0) : BM;
+        const int64_t rows_b = (N - n0) < BN ? (N - n0) : BN;
+        ra = buffer_rsrc(a.X + m0 * K, static_cast<uint32_t>(rows_a * K * 2));
+        rb = buffer_rsrc(a.W + n0 * K, static_cast<uint32_t>(rows_b * K * 2));
+    };
+
+    const int drow = lane >> 3;
+    const int dchunk = (lane & 7) ^ drow;
+    auto copy_a = [&](__amdgpu_buffer_rsrc_t r, int T, int slot) {
+        const uint32_t soff = static_cast<uint32_t>(T * ROWB);
+#pragma unroll
+        for (int j = 0; j < NCA; ++j) {
+            const int b = grp * (A_BLK / 2) + wg + 4 * j;
+            dma16_buf(r, static_cast<uint32_t>((b * 8 + drow) * K * 2 + dchunk * 16), soff, lds + slot * SLOT + b * 1024);
+        }
+    };
+    auto copy_b = [&](__amdgpu_buffer_rsrc_t r, int T, int slot) {
+        const uint32_t soff = static_cast<uint32_t>(T * ROWB);
+#pragma unroll
+        for (int j = 0; j < NCB; ++j) {
+            const int b = grp * (B_BLK / 2) + wg + 4 * j;
+            dma16_buf(r, static_cast<uint32_t>((b * 8 + drow) * K * 2 + dchunk * 16), soff, lds + slot * SLOT + b * 1024);
+        }
+    };
+    auto slot_add = [](int slot, int d) { return slot + d >= SLOTS ? slot + d - SLOTS : slot + d; };
+
+    const int fr = lane & 31, fq = lane >> 5;
+    const int sw = fr & 7;
+    auto frag = [&](const char *base, int row0, int p, int h) -> bf16x8 {
+        return *reinterpret_cast<const bf16x8 *>(base + (row0 + fr) * ROWB + (((4 * p + 2 * h + fq) ^ sw) << 4));
+    };
+
+    int64_t tile = blockIdx.x;
+    __amdgpu_buffer_rsrc_t ca, cb, na, nb;
+    resources(tile, ca, cb);
+    resources(tile + gridDim.x, na, nb);
+    // slot of A of the current k-range (half index 2g for the g-th k-range
+    // this workgroup handles, counted across tiles)
+    int s0 = 0;
+    copy_a(ca, 0, 0);
+    copy_b(cb, 0, 1);
+    copy_a(ca, 1, 2);
+    wait_vm<NCA>();
+    barrier_nofence();
+
+    for (; tile < G; tile += gridDim.x) {
+        int64_t m0, n0;
+        origin(tile, m0, n0);
+        float bias[FN];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int64_t n = n0 + wn * TN + j * 32 + fr;
+            bias[j] = ((a.epi & 1) && n < N) ? bf16_bits_to_f32(a.bias[n]) : 0.f;
+        }
+        f32x16 acc[FM][FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+        auto run = [&](auto grp_tag) {
+            constexpr int GRP = decltype(grp_tag)::value;
+            if (GRP == 1) barrier_nofence();
+            bf16x8 af[FM][2], bfr[FN][2];
+            for (int T = 0; T < KH; ++T) {
+                const char *sa = lds + s0 * SLOT, *sb = lds + slot_add(s0, 1) * SLOT;
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                        for (int i = 0; i < FM; ++i) af[i][h] = frag(sa, wm * TM + i * 32, p, h);
+#pragma unroll
+                        for (int j = 0; j < FN; ++j) bfr[j][h] = frag(sb, wn * TN + j * 32, p, h);
+                    }
+                    if (p == 0) {
+                        // B(T+1): this tile's, or the next tile's B(0)
+                        if (T + 1 < KH)
+                            copy_b(cb, T + 1, slot_add(s0, 3));
+                        else
+                            copy_b(nb, 0, slot_add(s0, 3));
+                    } else {
+                        // A(T+2): this tile's, or the next tile's A(0) / A(1)
+                        if (T + 2 < KH)
+                            copy_a(ca, T + 2, slot_add(s0, 4));
+                        else
+                            copy_a(na, T + 2 - KH, slot_add(s0, 4));
+                    }
+                    if (GRP == 1 && p == 1) {
+                        wait_vm<NCA>();  // A(T+1), B(T+1) landed (this wave's part)
+                        lds_wait_all();  // the next phase refills the slot of A(T)
+                    }
+                    barrier_nofence();
+                    lds_wait_all();
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+#pragma unroll
+                        for (int i = 0; i < FM; ++i)
+#pragma unroll
+                            for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16(af[i][h], bfr[j][h], acc[i][j]);
+                    if (GRP == 0 && p == 1) wait_vm<NCA>();
+                    barrier_nofence();
+                }
+                s0 = slot_add(s0, 2);
+            }
+            if (GRP == 0) barrier_nofence();
+        };
+        if (grp == 0)
+            run(std::integral_constant<int, 0>{});
+        else
+            run(std::integral_constant<int, 1>{});
+
+        // ---- epilogue.  The slots of the last k-range's A and B (s0 + 3,
+        // s0 + 4) are free once every wave's reads of it have landed; the
+        // next tile's A(0), B(0), A(1) are in the other three.
+        const bool full = (m0 + BM <= M) && (n0 + BN <= N) && (N % 8 == 0) && a.out == OUT_BF16 &&
+                          (reinterpret_cast<uintptr_t>(a.Y) % 16 == 0);
+        if (full) {
+            lds_wait_all();
+            barrier_nofence();
+            uint16_t *stage0 = reinterpret_cast<uint16_t *>(lds + slot_add(s0, 3) * SLOT);
+            uint16_t *stage1 = reinterpret_cast<uint16_t *>(lds + slot_add(s0, 4) * SLOT);
+            constexpr int CPR = BN / 8;
+            constexpr int NPASS = 2 * TM * CPR / 512;
+            static_assert(2 * TM * CPR % 512 == 0, "whole passes");
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                // round r: group r's two 64-row blocks (wave rows wm * 64)
+                if (grp == r) {
+                    uint16_t *t16 = (wm & 1) ? stage1 : stage0;
+                    if (a.epi & 2)
+                        stage_tile_bf16<BN, FM, FN, true>(t16, acc, bias, 0, wn * TN, lane);
+                    else
+                        stage_tile_bf16<BN, FM, FN, false>(t16, acc, bias, 0, wn * TN, lane);
+                }
+                lds_wait_all();
+                barrier_nofence();
+                u32x4 v[NPASS];
+#pragma unroll
+                for (int p = 0; p < NPASS; ++p) {
+                    const int c = tid + 512 * p, row = c / CPR, ch = c % CPR;  // row 0..127 of the round
+                    const uint16_t *t16 = (row >= TM) ? stage1 : stage0;
+                    const int rr = row & (TM - 1);
+                    v[p] = *reinterpret_cast<const u32x4 *>(t16 + rr * BN + stage_col(rr, ch * 8));
+                }
+#pragma unroll
+                for (int p = 0; p < NPASS; ++p) {
+                    const int c = tid + 512 * p, row = c / CPR, ch = c % CPR;
+                    *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.Y) + (m0 + r * 2 * TM + row) * N + n0 + ch * 8) =
+                        v[p];
+                }
+                lds_wait_all();
+                barrier_nofence();
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int64_t n = n0 + wn * TN + j * 32 + fr;
+                if (n >= N) continue;
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int64_t m = m0 + wm * TM + i * 32 + 8 * (v / 4) + 4 * fq + (v % 4);
+                        if (m < M) store_out(a.Y, a.out, m * N + n, apply_epilogue(acc[i][j][v], a.epi, bias[j]));
+                    }
+            }
+        }
+        ca = na;
+        cb = nb;
+        resources(tile + 2 * static_cast<int64_t>(gridDim.x), na, nb);
+    }
+    // the copies issued for the tile after the last one (empty resource)
+    // still write LDS: drain them before the workgroup ends
+    wait_vm<0>();
+}
+
 // One list drives both compilation passes (device: kernel instantiation,
 // host: launch table).
 #define PROJ_GEMM_VARIANTS(X)                                                                    \
@@ -660,6 +894,8 @@ PROJ_GEMM_PP_VARIANTS(PROJ_GEMM_PP_INST)
 #define PROJ_GEMM_PP64_VARIANTS(X) X(256, 4) X(256, 8) X(192, 4)
 #define PROJ_GEMM_PP64_INST(BN, GM) template __global__ void gemm_pp64_kernel<BN, GM>(Args);
 PROJ_GEMM_PP64_VARIANTS(PROJ_GEMM_PP64_INST)
+#define PROJ_GEMM_PP64P_INST(BN, GM) template __global__ void gemm_pp64p_kernel<BN, GM>(Args);
+PROJ_GEMM_PP64_VARIANTS(PROJ_GEMM_PP64P_INST)
 
 #ifndef __HIP_DEVICE_COMPILE__
 template <int BM, int BN, int BK, int WM, int WN, int GM>
@@ -717,14 +953,44 @@ static hipError_t launch_gemm_pp64(const Args &a, hipStream_t st) {
     return hipGetLastError();
 }
 
+// compute units of the device the library was prepared on (the persistent
+// kernel launches one workgroup per CU)
+static int g_num_cus = 0;
+
+template <int BN, int GM>
+static hipError_t prepare_gemm_pp64p() {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&g_num_cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    auto fn = gemm_pp64p_kernel<BN, GM>;
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               5 * 32 * 1024);
+}
+
+// K < 128 (one k-range) runs the non-persistent kernel
+template <int BN, int GM>
+static hipError_t launch_gemm_pp64p(const Args &a, hipStream_t st) {
+    if (a.K < 128) return launch_gemm_pp64<BN, GM>(a, st);
+    const int64_t G = ((a.M + 255) / 256) * ((a.N + BN - 1) / BN);
+    if (G <= 0 || G > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const int64_t cus = g_num_cus > 0 ? g_num_cus : 256;
+    const int64_t grid = G < cus ? G : cus;
+    hipLaunchKernelGGL((gemm_pp64p_kernel<BN, GM>), dim3(static_cast<unsigned>(grid)), dim3(512), 5 * 32 * 1024, st, a);
+    return hipGetLastError();
+}
+
 #define PROJ_GEMM_ENTRY(BM, BN, WM, WN, GM) \
     {"gemm", BM, BN, 64, 64, WM, WN, GM, 0, &launch_gemm<BM, BN, 64, WM, WN, GM>, &prepare_gemm<BM, BN, 64, WM, WN, GM>},
 #define PROJ_GEMM_PP_ENTRY(BN, GM) \
     {"gemmpp", 256, BN, 32, 32, 4, 2, GM, kRingMaxK, &launch_gemm_pp<BN, GM>, &prepare_gemm_pp<BN, GM>},
 #define PROJ_GEMM_PP64_ENTRY(BN, GM) \
     {"gemmpp64", 256, BN, 64, 64, 4, 2, GM, kRingMaxK, &launch_gemm_pp64<BN, GM>, &prepare_gemm_pp64<BN, GM>},
+#define PROJ_GEMM_PP64P_ENTRY(BN, GM) \
+    {"gemmpp64p", 256, BN, 64, 64, 4, 2, GM, kRingMaxK, &launch_gemm_pp64p<BN, GM>, &prepare_gemm_pp64p<BN, GM>},
 const GemmVariant kGemmVariants[] = {PROJ_GEMM_VARIANTS(PROJ_GEMM_ENTRY) PROJ_GEMM_PP_VARIANTS(PROJ_GEMM_PP_ENTRY)
-                                         PROJ_GEMM_PP64_VARIANTS(PROJ_GEMM_PP64_ENTRY)};
+                                         PROJ_GEMM_PP64_VARIANTS(PROJ_GEMM_PP64_ENTRY)
+                                             PROJ_GEMM_PP64_VARIANTS(PROJ_GEMM_PP64P_ENTRY)};
 const int kNumGemmVariants = sizeof(kGemmVariants) / sizeof(kGemmVariants[0]);
 #endif
 

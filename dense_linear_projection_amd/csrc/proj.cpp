@@ -178,15 +178,19 @@ Candidate default_candidate(const Key &k) {
         return nullptr;
     };
     if (mt_for(k.M) > 0) {
-        // 32 rows per workgroup, 256-byte row segments, 4 stages in flight,
-        // and the smallest split count that gives every CU a workgroup
-        for (const Candidate &x : c) {
-            if (x.kind != KIND_STREAM) continue;
-            const StreamVariant &v = kStreamVariants[x.variant];
-            if (v.nt != 2 || v.kc != 128 || v.depth != 5 || v.waves != 4 || v.wnt) continue;
-            if (((k.N + 31) / 32) * x.splits >= 256 || x.splits == 8) return x;
-        }
+        // 32 rows per workgroup, 256-byte row segments, non-temporal W if
+        // such a variant exists for this M (else 5 stages in flight), and
+        // the smallest split count that gives every CU a workgroup
+        for (int pass = 0; pass < 2; ++pass)
+            for (const Candidate &x : c) {
+                if (x.kind != KIND_STREAM) continue;
+                const StreamVariant &v = kStreamVariants[x.variant];
+                if (v.nt != 2 || v.kc != 128 || v.waves != 4) continue;
+                if (pass == 0 ? !v.wnt : (v.wnt || v.depth != 5)) continue;
+                if (((k.N + 31) / 32) * x.splits >= 256 || x.splits == 8) return x;
+            }
     }
+    if (const Candidate *g = find("gemmpp64_256x256x64_w4x2_g4")) return *g;
     if (const Candidate *g = find("gemmpp_256x256x32_w4x2_g4")) return *g;
     if (const Candidate *g = find("gemm_256x256x64_w2x2_g4")) return *g;
     for (const Candidate &x : c)

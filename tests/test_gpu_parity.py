@@ -83,6 +83,37 @@ def test_every_candidate_within_tolerance_random(ctx, shape):
             assert rep["ok"], "%s epi=%d: %s" % (name, epi, rep)
 
 
+def test_persistent_tile_walk(ctx):
+    """More 256-row tiles than CUs, so persistent workgroups walk several
+    tiles with the LDS ring running on across them; a ragged last tile row
+    takes the element-wise epilogue between full tiles.  Integer inputs:
+    every large-M candidate bit-exact; then GELU within tolerance."""
+    M, N, K = 4196, 4352, 128
+    X = synth.integer_bf16((M, K), -8, 8, 41)
+    W = synth.integer_bf16((N, K), -8, 8, 42)
+    b = synth.integer_bf16((N,), -64, 64, 43)
+    Xd, Wd, bd = dev_bf16(X), dev_bf16(W), dev_bf16(b)
+    for epi, out in ((oracle.EPI_NONE, oracle.OUT_BF16), (oracle.EPI_BIAS, oracle.OUT_BF16),
+                     (oracle.EPI_BIAS, oracle.OUT_F32)):
+        r, _ = oracle.reference(X, W, b if epi & 1 else None, epi, out)
+        names = candidate_names(M, N, K, epi, out)
+        assert any(n.startswith("gemmpp64p") for n in names)
+        for i, name in enumerate(names):
+            u = run_candidate(ctx, i, Xd, Wd, bd, epi, M, N, K, out)
+            bad = np.argwhere(u != r)
+            assert bad.size == 0, "%s epi=%d out=%d: %d mismatches, first at %s: %r vs %r" % (
+                name, epi, out, len(bad), bad[0], u[tuple(bad[0])], r[tuple(bad[0])])
+    Xr, Wr, br = synth.make_inputs(M, N, K, True, 44)
+    Xd, Wd, bd = dev_bf16(Xr), dev_bf16(Wr), dev_bf16(br)
+    r, _ = oracle.reference(Xr, Wr, br, oracle.EPI_BIAS_GELU, oracle.OUT_BF16)
+    for i, name in enumerate(candidate_names(M, N, K, oracle.EPI_BIAS_GELU, oracle.OUT_BF16)):
+        if not name.startswith("gemmpp64"):
+            continue
+        u = run_candidate(ctx, i, Xd, Wd, bd, oracle.EPI_BIAS_GELU, M, N, K, oracle.OUT_BF16)
+        rep = compare.check(u, r)
+        assert rep["ok"], "%s: %s" % (name, rep)
+
+
 @pytest.mark.parametrize("M", [1, 15, 16, 17, 63, 64, 65, 127, 128, 129])
 def test_token_counts_around_tile_edges(ctx, M):
     """Tuned plan (proj_run) at token counts on both sides of tile edges."""
