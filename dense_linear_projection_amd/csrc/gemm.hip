@@ -19,7 +19,7 @@
 //   * gemm_pp64_kernel: the same with 128-byte LDS rows (k copied 64 at a
 //     time) in a ring of operand halves (K a multiple of 64);
 //   * gemm_pp64p_kernel: its persistent form, one workgroup per CU walking
-//     tiles with the ring running on across them.
+//     tiles with the ring running on across them, on 16x16x32 matrix ops.
 // Both operands are K-major in memory (X[m, k], W[n, k]) and are staged the
 // same way: global -> LDS copies without a register round trip (one
 // instruction moves 64 lanes x 16 bytes), with 16-byte chunks XOR-swizzled by
@@ -656,6 +656,34 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 }
 
+// stage_tile_bf16 for 16x16x32 accumulators: lane l holds column l%16 and
+// rows 4 (l/16) + 0..3 of each 16x16 block.
+template <int BN, int FM, int FN, bool GELU>
+__device__ __forceinline__ void stage_tile16_bf16(uint16_t *t16, const f32x4 (&acc)[FM][FN], const float (&bias)[FN],
+                                                  int row0, int col0, int lane) {
+    const int fr = lane & 15, fg = lane >> 4;
+    const bool odd = lane & 1;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const int col = col0 + j * 16 + (fr & ~1);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int v = 0; v < 4; v += 2) {
+                float e0 = acc[i][j][v] + bias[j], e1 = acc[i][j][v + 1] + bias[j];
+                if (GELU) {
+                    e0 = gelu_tanh_fast(e0);
+                    e1 = gelu_tanh_fast(e1);
+                }
+                const float send = odd ? e0 : e1;
+                const float recv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, true));
+                const float lo = odd ? recv : e0, hi = odd ? e1 : recv;
+                const int row = row0 + i * 16 + 4 * fg + v + (odd ? 1 : 0);
+                *reinterpret_cast<uint32_t *>(t16 + row * BN + stage_col(row, col)) = pack_bf16x2(lo, hi);
+            }
+    }
+}
+
 // Persistent form of gemm_pp64_kernel: one workgroup per CU walks tiles
 // blockIdx.x, blockIdx.x + gridDim.x, ...  The LDS ring runs on across tiles
 // (the copies the last k-ranges of a tile would make past K fetch the next
@@ -666,11 +694,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // first halves): group 0's rows 0..127 first, then group 1's rows 128..255,
 // each 64-row wave block in one slot.  Needs K >= 128 (two k-ranges), so
 // that the ring's look-ahead stays within the next tile.
+// Matrix ops are 16x16x32 (each wave 4 x BN/32 blocks of 16 x 16, one
+// fragment per 16 rows and k-step): with the same LDS traffic this form ran
+// 6% faster than 32x32x16 blocks on the M=4096, K=N=8192 GEMM.
 template <int BN, int GM>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_pp64p_kernel(Args a) {
     constexpr int BM = 256, NW = 8, SLOTS = 5, SLOT = 32 * 1024;
     constexpr int TM = 64, TN = BN / 2;
-    constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr int FM = TM / 16, FN = TN / 16;  // 16x16 blocks
     constexpr int ROWB = 128;
     constexpr int A_BLK = BM / 8, B_BLK = BN / 8;
     constexpr int NCA = A_BLK / NW, NCB = B_BLK / NW;
@@ -737,10 +768,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     };
     auto slot_add = [](int slot, int d) { return slot + d >= SLOTS ? slot + d - SLOTS : slot + d; };
 
-    const int fr = lane & 31, fq = lane >> 5;
-    const int sw = swz128(fr);  // row0 is a multiple of 32
-    auto frag = [&](const char *base, int row0, int p, int h) -> bf16x8 {
-        return *reinterpret_cast<const bf16x8 *>(base + (row0 + fr) * ROWB + (((4 * p + 2 * h + fq) ^ sw) << 4));
+    // 16x16x32 fragments: lane l reads row row0 + l%16, chunk 4p + l/16
+    const int fr = lane & 15, fg = lane >> 4;
+    const int sw = swz128(fr);  // row0 is a multiple of 16
+    auto frag = [&](const char *base, int row0, int p) -> bf16x8 {
+        return *reinterpret_cast<const bf16x8 *>(base + (row0 + fr) * ROWB + (((4 * p + fg) ^ sw) << 4));
     };
 
     int64_t tile = blockIdx.x;
@@ -762,32 +794,27 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         float bias[FN];
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-            const int64_t n = n0 + wn * TN + j * 32 + fr;
+            const int64_t n = n0 + wn * TN + j * 16 + fr;
             bias[j] = ((a.epi & 1) && n < N) ? bf16_bits_to_f32(a.bias[n]) : 0.f;
         }
-        f32x16 acc[FM][FN];
+        f32x4 acc[FM][FN];
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+            for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
         auto run = [&](auto grp_tag) {
             constexpr int GRP = decltype(grp_tag)::value;
             if (GRP == 1) barrier_nofence();
-            bf16x8 af[FM][2], bfr[FN][2];
+            bf16x8 af[FM], bfr[FN];
             for (int T = 0; T < KH; ++T) {
                 const char *sa = lds + s0 * SLOT, *sb = lds + slot_add(s0, 1) * SLOT;
 #pragma unroll
                 for (int p = 0; p < 2; ++p) {
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
+                    for (int i = 0; i < FM; ++i) af[i] = frag(sa, wm * TM + i * 16, p);
 #pragma unroll
-                        for (int i = 0; i < FM; ++i) af[i][h] = frag(sa, wm * TM + i * 32, p, h);
-#pragma unroll
-                        for (int j = 0; j < FN; ++j) bfr[j][h] = frag(sb, wn * TN + j * 32, p, h);
-                    }
+                    for (int j = 0; j < FN; ++j) bfr[j] = frag(sb, wn * TN + j * 16, p);
                     if (p == 0) {
                         // B(T+1): this tile's, or the next tile's B(0)
                         if (T + 1 < KH)
@@ -809,11 +836,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     lds_wait_all();
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int h = 0; h < 2; ++h)
+                    for (int i = 0; i < FM; ++i)
 #pragma unroll
-                        for (int i = 0; i < FM; ++i)
-#pragma unroll
-                            for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16(af[i][h], bfr[j][h], acc[i][j]);
+                        for (int j = 0; j < FN; ++j) acc[i][j] = mfma16x16x32(af[i], bfr[j], acc[i][j]);
                     if (GRP == 0 && p == 1) wait_vm<NCA>();
                     barrier_nofence();
                 }
@@ -845,9 +870,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 if (grp == r) {
                     uint16_t *t16 = (wm & 1) ? stage1 : stage0;
                     if (a.epi & 2)
-                        stage_tile_bf16<BN, FM, FN, true>(t16, acc, bias, 0, wn * TN, lane);
+                        stage_tile16_bf16<BN, FM, FN, true>(t16, acc, bias, 0, wn * TN, lane);
                     else
-                        stage_tile_bf16<BN, FM, FN, false>(t16, acc, bias, 0, wn * TN, lane);
+                        stage_tile16_bf16<BN, FM, FN, false>(t16, acc, bias, 0, wn * TN, lane);
                 }
                 lds_wait_all();
                 barrier_nofence();
@@ -871,13 +896,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         } else {
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
-                const int64_t n = n0 + wn * TN + j * 32 + fr;
+                const int64_t n = n0 + wn * TN + j * 16 + fr;
                 if (n >= N) continue;
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int64_t m = m0 + wm * TM + i * 32 + 8 * (v / 4) + 4 * fq + (v % 4);
+                    for (int v = 0; v < 4; ++v) {
+                        const int64_t m = m0 + wm * TM + i * 16 + 4 * fg + v;
                         if (m < M) store_out(a.Y, a.out, m * N + n, apply_epilogue(acc[i][j][v], a.epi, bias[j]));
                     }
             }
