@@ -656,16 +656,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 }
 
-// stage_tile_bf16 for 16x16x32 accumulators: lane l holds column l%16 and
-// rows 4 (l/16) + 0..3 of each 16x16 block.
+// Write a wave's 16x16x32-layout accumulators (FM x FN blocks at tile rows
+// row0 + 16 i, columns col0 + 16 j), after bias and the optional GELU, into
+// the bf16 staging tile t16[rows][BN] (columns placed by stage_col).  A lane holds one column and rows 4 (l/16) + 0..3 of each
+// block: each pair of adjacent rows is converted in one packed conversion
+// and written as two 16-bit stores, which keeps the vector ALU work (the
+// bound of a GELU epilogue) at the GELU itself.
 template <int BN, int FM, int FN, bool GELU>
 __device__ __forceinline__ void stage_tile16_bf16(uint16_t *t16, const f32x4 (&acc)[FM][FN], const float (&bias)[FN],
                                                   int row0, int col0, int lane) {
     const int fr = lane & 15, fg = lane >> 4;
-    const bool odd = lane & 1;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-        const int col = col0 + j * 16 + (fr & ~1);
+        const int col = col0 + j * 16 + fr;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -675,11 +678,10 @@ __device__ __forceinline__ void stage_tile16_bf16(uint16_t *t16, const f32x4 (&a
                     e0 = gelu_tanh_fast(e0);
                     e1 = gelu_tanh_fast(e1);
                 }
-                const float send = odd ? e0 : e1;
-                const float recv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, true));
-                const float lo = odd ? recv : e0, hi = odd ? e1 : recv;
-                const int row = row0 + i * 16 + 4 * fg + v + (odd ? 1 : 0);
-                *reinterpret_cast<uint32_t *>(t16 + row * BN + stage_col(row, col)) = pack_bf16x2(lo, hi);
+                const uint32_t p = pack_bf16x2(e0, e1);
+                const int row = row0 + i * 16 + 4 * fg + v;
+                t16[row * BN + stage_col(row, col)] = static_cast<uint16_t>(p);
+                t16[(row + 1) * BN + stage_col(row + 1, col)] = static_cast<uint16_t>(p >> 16);
             }
     }
 }
