@@ -430,7 +430,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int p = 0; p < NPASS; ++p) {
             const int c = tid + 512 * p, row = c / CPR, ch = c % CPR;
-            *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.Y) + (m0 + row) * N + n0 + ch * 8) = v[p];
+            __builtin_nontemporal_store(v[p], reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.Y) + (m0 + row) * N + n0 + ch * 8));
         }
     } else {
 #pragma unroll
@@ -638,7 +638,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int p = 0; p < NPASS; ++p) {
             const int c = tid + 512 * p, row = c / CPR, ch = c % CPR;
-            *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.Y) + (m0 + row) * N + n0 + ch * 8) = v[p];
+            __builtin_nontemporal_store(v[p], reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.Y) + (m0 + row) * N + n0 + ch * 8));
         }
     } else {
 #pragma unroll
@@ -889,8 +889,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                 for (int p = 0; p < NPASS; ++p) {
                     const int c = tid + 512 * p, row = c / CPR, ch = c % CPR;
-                    *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.Y) + (m0 + r * 2 * TM + row) * N + n0 + ch * 8) =
-                        v[p];
+                    __builtin_nontemporal_store(
+                        v[p], reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.Y) + (m0 + r * 2 * TM + row) * N + n0 + ch * 8));
                 }
                 lds_wait_all();
                 barrier_nofence();
