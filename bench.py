@@ -208,6 +208,116 @@ def cpu_baseline(w, X, W, b, min_seconds: float):
     }
 
 
+def sweep(args) -> int:
+    """The worklog's thirty-shape set (synth.sweep_shapes): for every shape,
+    the tuned plan replayed from a HIP graph over rotating buffer sets (the
+    main bench's protocol), and beside it torch's matmul (hipBLASLt) replayed
+    from a torch CUDA graph the same way -- context, not a target.  Per load
+    the five shapes' times are summed; the loads' torch/ours ratios are
+    combined by geometric mean, as the worklog scores (section "A quick guide
+    to the numbers I'll be showing").  Prints one JSON line."""
+    import math
+    import numpy as np
+    import torch
+
+    import dense_linear_projection_amd as dlp
+    import synth
+
+    if not os.path.exists(dlp.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    ctx = dlp.proj_create(0)
+    stream = torch.cuda.Stream()
+    to_dev = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    steps = args.sweep_steps
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+
+    def time_replays(launch, R):
+        for _ in range(3):
+            launch()
+        stream.synchronize()
+        reps = max(1, steps // R)
+        e0.record(stream)
+        for _ in range(reps):
+            launch()
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * R)
+
+    rows = []
+    for sh in synth.sweep_shapes():
+        row = {"name": sh.name, "family": sh.family, "M": sh.M, "N": sh.N, "K": sh.K}
+        if sh.fp32_weights:
+            row["status"] = "fp32-weight router: not built"
+            rows.append(row)
+            continue
+        X0, W0 = synth.sweep_inputs(sh)
+        set_bytes = sh.alg_bytes()
+        P = min(16, max(1, -(-(2 * LLC_BYTES) // set_bytes)))
+        R = max(P, 64 // P * P)
+        Xs = [to_dev(X0)] + [to_dev(synth.sweep_inputs(sh, 100 * p)[0]) for p in range(1, P)]
+        Wd = to_dev(W0)
+        Ws = [Wd] + [Wd.clone() for _ in range(1, P)]
+        Ys = [torch.empty((sh.M, sh.N), dtype=torch.bfloat16, device=dev) for _ in range(P)]
+        with torch.cuda.stream(stream):
+            for p in range(P):
+                dlp.proj_run(ctx, Xs[p], Ws[p], None, dlp.EPI_NONE, Ys[p], stream=stream)
+        stream.synchronize()
+        plan = dlp.proj_get_plan(ctx, sh.M, sh.N, sh.K, dlp.EPI_NONE, synth.OUT_BF16)
+        idx = [i % P for i in range(R)]
+        g = dlp.proj_graph_capture(ctx, [Xs[i] for i in idx], [Ws[i] for i in idx], None, [Ys[i] for i in idx],
+                                   dlp.EPI_NONE, stream=stream)
+        us = time_replays(lambda: dlp.proj_graph_launch(g, stream=stream), R)
+        dlp.proj_graph_destroy(g)
+        # torch: the same products into separate outputs, captured once
+        Yt = [torch.empty_like(y) for y in Ys]
+        with torch.cuda.stream(stream):
+            for p in range(P):
+                torch.matmul(Xs[p], Ws[p].t(), out=Yt[p])
+        stream.synchronize()
+        ref = Yt[0].clone()
+        tg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(tg, stream=stream):
+            for i in idx:
+                torch.matmul(Xs[i], Ws[i].t(), out=Yt[i])
+        def replay_on_stream():
+            with torch.cuda.stream(stream):
+                tg.replay()
+
+        torch_us = time_replays(replay_on_stream, R)
+        stream.synchronize()
+        torch_ok = bool(torch.equal(Yt[0], ref))
+        del tg
+        sec = us * 1e-6
+        row.update({"plan": plan.split(" ")[0], "us": round(us, 3),
+                    "gbs": round(sh.alg_bytes() / sec / 1e9, 1),
+                    "hbm_frac": round(sh.alg_bytes() / sec / 1e9 / HBM_PEAK_GBS, 4),
+                    "tflops": round(sh.alg_flops() / sec / 1e12, 2),
+                    "torch_us": round(torch_us, 3), "torch_replay_matches_eager": torch_ok,
+                    "torch_over_ours": round(torch_us / us, 4)})
+        rows.append(row)
+        print(json.dumps(row), file=sys.stderr, flush=True)
+        del Xs, Ws, Ys, Yt, Wd
+        torch.cuda.empty_cache()
+    dlp.proj_destroy(ctx)
+
+    loads = []
+    for M in synth.SWEEP_LOADS:
+        rs = [r for r in rows if r["M"] == M and "us" in r]
+        ours, theirs = sum(r["us"] for r in rs), sum(r["torch_us"] for r in rs)
+        loads.append({"M": M, "shapes_timed": len(rs), "us_sum": round(ours, 3), "torch_us_sum": round(theirs, 3),
+                      "torch_over_ours": round(theirs / ours, 4)})
+    geo = math.exp(sum(math.log(l["torch_over_ours"]) for l in loads) / len(loads))
+    print(json.dumps({"metric": "thirty-shape sweep: per-load time, torch (hipBLASLt) time over ours",
+                      "shapes": rows, "loads": loads, "geomean_torch_over_ours": round(geo, 4),
+                      "note": "loads sum the bf16 shapes that are built; the fp32-weight router is not included"}),
+          flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -221,6 +331,9 @@ def main() -> int:
                     help="only run a plain copy of known size (for counter scaling)")
     ap.add_argument("--ingest", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="write profiles/counters_<workload>.json from rocprofv3 --pmc outputs")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the thirty-shape set (per load; torch alongside as context) instead of one workload")
+    ap.add_argument("--sweep-steps", type=int, default=400, help="calls timed per shape in --sweep")
     ap.add_argument("--plans", nargs="+", default=[],
                     help="for --ingest: one-pass stream plans to take counters for")
     args = ap.parse_args()
@@ -228,6 +341,8 @@ def main() -> int:
         return ingest_counters(args)
     if args.copy_calibration:
         return copy_calibration()
+    if args.sweep:
+        return sweep(args)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the projection path is single-GPU in this build "

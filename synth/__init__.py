@@ -59,6 +59,62 @@ WORKLOADS = [
 ]
 
 
+# The thirty-shape set of the worklog (section "The same calculation shows up
+# in different sizes"): six loads -- decode with 1, 16 or 32 token rows,
+# verification with 8, 128 or 256 -- times five projection families.  The
+# projections have no bias (the worklog's plain Y = X W^T); bf16 weights give
+# bf16 outputs.  The router's weights are fp32 and its output fp32.  The
+# unpooler's smaller output slice is read as applying to the loads of at most
+# 32 token rows.
+SWEEP_LOADS = (1, 16, 32, 8, 128, 256)
+
+
+@dataclass(frozen=True)
+class SweepShape:
+    index: int
+    family: str
+    M: int
+    N: int
+    K: int
+    fp32_weights: bool
+
+    @property
+    def name(self) -> str:
+        return "%s_m%d_n%d_k%d" % (self.family, self.M, self.N, self.K)
+
+    def alg_bytes(self) -> int:
+        """X and W read once (W in its stored format), Y written once."""
+        w_b = 4 if self.fp32_weights else 2
+        y_b = 4 if self.fp32_weights else 2
+        return 2 * self.M * self.K + w_b * self.N * self.K + y_b * self.M * self.N
+
+    def alg_flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+
+def sweep_shapes():
+    out = []
+    for M in SWEEP_LOADS:
+        fams = [("qkv_gate", 2304, 8192, False), ("output", 8192, 1024, False), ("pooler", 4096, 8192, False),
+                ("unpooler", 1024 if M <= 32 else 8192, 4096, False), ("router", 256, 8192, True)]
+        for fam, N, K, f32w in fams:
+            out.append(SweepShape(len(out), fam, M, N, K, f32w))
+    return out
+
+
+def sweep_inputs(s: SweepShape, offset: int = 0):
+    """(X, W) for a sweep shape: X bf16 bits ~ N(0, 1); W ~ N(0, 1/K) as bf16
+    bits, or as float32 values for fp32-weight shapes.  Seeds 5000 + index
+    (X) and 6000 + index (W)."""
+    X = normal_bf16((s.M, s.K), 1.0, 5000 + s.index + offset)
+    if not s.fp32_weights:
+        return X, normal_bf16((s.N, s.K), float(1.0 / np.sqrt(s.K)), 6000 + s.index + offset)
+    rng = np.random.Generator(np.random.PCG64(6000 + s.index + offset))
+    W = rng.standard_normal((s.N, s.K), dtype=np.float32)
+    W *= np.float32(1.0 / np.sqrt(s.K))
+    return X, W
+
+
 def f32_to_bf16_bits(a: np.ndarray, out: np.ndarray | None = None) -> np.ndarray:
     """Round float32 samples to bf16 bit patterns (nearest, ties to even).
     Only used to produce inputs; the samples must be finite."""

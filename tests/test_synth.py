@@ -35,3 +35,20 @@ def test_bf16_rounding_of_inputs():
     # halfway cases go to the even neighbour
     v = np.array([1.00390625, 1.01171875, -1.00390625], dtype=np.float32)
     assert synth.f32_to_bf16_bits(v).tolist() == [0x3F80, 0x3F82, 0xBF80]
+
+
+def test_sweep_shapes_follow_the_table():
+    shapes = synth.sweep_shapes()
+    assert len(shapes) == 30
+    assert sorted({s.M for s in shapes}) == [1, 8, 16, 32, 128, 256]
+    fam = {(s.family, s.M): s for s in shapes}
+    for M in synth.SWEEP_LOADS:
+        assert (fam[("qkv_gate", M)].N, fam[("qkv_gate", M)].K) == (2304, 8192)
+        assert (fam[("output", M)].N, fam[("output", M)].K) == (8192, 1024)
+        assert (fam[("pooler", M)].N, fam[("pooler", M)].K) == (4096, 8192)
+        assert fam[("unpooler", M)].K == 4096 and fam[("unpooler", M)].N == (1024 if M <= 32 else 8192)
+        r = fam[("router", M)]
+        assert (r.N, r.K, r.fp32_weights) == (256, 8192, True)
+    X, W = synth.sweep_inputs(fam[("router", 1)])
+    assert X.dtype == np.uint16 and W.dtype == np.float32 and W.shape == (256, 8192)
+    assert abs(W.std() * np.sqrt(8192) - 1.0) < 0.02
