@@ -696,11 +696,15 @@ __device__ __forceinline__ void stage_tile16_bf16(uint16_t *t16, const f32x4 (&a
 // first halves): group 0's rows 0..127 first, then group 1's rows 128..255,
 // each 64-row wave block in one slot.  Needs K >= 128 (two k-ranges), so
 // that the ring's look-ahead stays within the next tile.
+// With S > 1 the work items are (tile, K split) pairs -- for token counts
+// that give too few tiles to fill the CUs -- and each item writes its fp32
+// partial to the workspace, which the split-K reduction kernel sums with the
+// epilogue; a split covers at least two k-ranges.
 // Matrix ops are 16x16x32 (each wave 4 x BN/32 blocks of 16 x 16, one
 // fragment per 16 rows and k-step): with the same LDS traffic this form ran
 // 6% faster than 32x32x16 blocks on the M=4096, K=N=8192 GEMM.
 template <int BN, int GM>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_pp64p_kernel(Args a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_pp64p_kernel(Args a, int S) {
     constexpr int BM = 256, NW = 8, SLOTS = 5, SLOT = 32 * 1024;
     constexpr int TM = 64, TN = BN / 2;
     constexpr int FM = TM / 16, FN = TN / 16;  // 16x16 blocks
@@ -721,26 +725,38 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     const int64_t G = tiles_m * tiles_n;
     const int KH = static_cast<int>(K / 64);
-
-    // tile -> origin: XCD-contiguous renumbering (a workgroup's tiles all
-    // lie on its XCD, since gridDim.x is a multiple of 8), then GM-row groups
-    auto origin = [&](int64_t tile, int64_t &m0, int64_t &n0) {
-        int64_t L = tile;
-        if (G % 8 == 0) L = (L % 8) * (G / 8) + L / 8;
+    // work items: (tile, K split) pairs, item = tile * S + split; a split
+    // covers k-ranges [KH * split / S, KH * (split + 1) / S), at least two
+    const int64_t GS = G * S;
+    auto krange = [&](int64_t item, int &kb, int &ke) {
+        const int sp = static_cast<int>(item % S);
+        kb = static_cast<int>((static_cast<int64_t>(KH) * sp) / S);
+        ke = static_cast<int>((static_cast<int64_t>(KH) * (sp + 1)) / S);
+    };
+    // item -> tile origin: XCD-contiguous renumbering of the items (a
+    // workgroup's items all lie on its XCD, since gridDim.x is a multiple of
+    // 8), then GM-row groups of tiles
+    auto remap = [&](int64_t item) { return GS % 8 == 0 ? (item % 8) * (GS / 8) + item / 8 : item; };
+    auto origin = [&](int64_t item, int64_t &m0, int64_t &n0) {
+        const int64_t L = remap(item) / S;
         const int64_t per_group = GM * tiles_n;
         const int64_t first_m = (L / per_group) * GM;
         const int64_t gsz = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
         m0 = (first_m + (L % per_group) % gsz) * BM;
         n0 = ((L % per_group) / gsz) * BN;
     };
-    // buffer resources over a tile's valid X and W rows (empty past the last tile)
-    auto resources = [&](int64_t tile, __amdgpu_buffer_rsrc_t &ra, __amdgpu_buffer_rsrc_t &rb) {
-        if (tile >= G) {
+    // buffer resources over an item's tile's valid X and W rows, and the
+    // item's first k-range (empty resources past the last item)
+    auto resources = [&](int64_t item, __amdgpu_buffer_rsrc_t &ra, __amdgpu_buffer_rsrc_t &rb, int &kb) {
+        if (item >= GS) {
             ra = rb = buffer_rsrc(a.X, 0);
+            kb = 0;
             return;
         }
+        int ke;
+        krange(remap(item), kb, ke);
         int64_t m0, n0;
-        origin(tile, m0, n0);
+        origin(item, m0, n0);
         const int64_t rows_a = (M - m0) < BM ? (M - m0) : BM;
         const int64_t rows_b = (N - n0) < BN ? (N - n0) : BN;
         ra = buffer_rsrc(a.X + m0 * K, static_cast<uint32_t>(rows_a * K * 2));
@@ -777,22 +793,26 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         return *reinterpret_cast<const bf16x8 *>(base + (row0 + fr) * ROWB + (((4 * p + fg) ^ sw) << 4));
     };
 
-    int64_t tile = blockIdx.x;
+    int64_t item = blockIdx.x;
     __amdgpu_buffer_rsrc_t ca, cb, na, nb;
-    resources(tile, ca, cb);
-    resources(tile + gridDim.x, na, nb);
+    int ckb, nkb;
+    resources(item, ca, cb, ckb);
+    resources(item + gridDim.x, na, nb, nkb);
     // slot of A of the current k-range (half index 2g for the g-th k-range
-    // this workgroup handles, counted across tiles)
+    // this workgroup handles, counted across items)
     int s0 = 0;
-    copy_a(ca, 0, 0);
-    copy_b(cb, 0, 1);
-    copy_a(ca, 1, 2);
+    copy_a(ca, ckb, 0);
+    copy_b(cb, ckb, 1);
+    copy_a(ca, ckb + 1, 2);
     wait_vm<NCA>();
     barrier_nofence();
 
-    for (; tile < G; tile += gridDim.x) {
+    for (; item < GS; item += gridDim.x) {
         int64_t m0, n0;
-        origin(tile, m0, n0);
+        origin(item, m0, n0);
+        int kb, ke;
+        krange(remap(item), kb, ke);
+        const int split = static_cast<int>(remap(item) % S);
         float bias[FN];
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
@@ -809,7 +829,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             constexpr int GRP = decltype(grp_tag)::value;
             if (GRP == 1) barrier_nofence();
             bf16x8 af[FM], bfr[FN];
-            for (int T = 0; T < KH; ++T) {
+            for (int T = kb; T < ke; ++T) {
                 const char *sa = lds + s0 * SLOT, *sb = lds + slot_add(s0, 1) * SLOT;
 #pragma unroll
                 for (int p = 0; p < 2; ++p) {
@@ -818,17 +838,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                     for (int j = 0; j < FN; ++j) bfr[j] = frag(sb, wn * TN + j * 16, p);
                     if (p == 0) {
-                        // B(T+1): this tile's, or the next tile's B(0)
-                        if (T + 1 < KH)
+                        // B(T+1): this item's, or the next item's first
+                        if (T + 1 < ke)
                             copy_b(cb, T + 1, slot_add(s0, 3));
                         else
-                            copy_b(nb, 0, slot_add(s0, 3));
+                            copy_b(nb, nkb, slot_add(s0, 3));
                     } else {
-                        // A(T+2): this tile's, or the next tile's A(0) / A(1)
-                        if (T + 2 < KH)
+                        // A(T+2): this item's, or the next item's first two
+                        if (T + 2 < ke)
                             copy_a(ca, T + 2, slot_add(s0, 4));
                         else
-                            copy_a(na, T + 2 - KH, slot_add(s0, 4));
+                            copy_a(na, nkb + T + 2 - ke, slot_add(s0, 4));
                     }
                     if (GRP == 1 && p == 1) {
                         wait_vm<NCA>();  // A(T+1), B(T+1) landed (this wave's part)
@@ -858,7 +878,23 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // next tile's A(0), B(0), A(1) are in the other three.
         const bool full = (m0 + BM <= M) && (n0 + BN <= N) && (N % 8 == 0) && a.out == OUT_BF16 &&
                           (reinterpret_cast<uintptr_t>(a.Y) % 16 == 0);
-        if (full) {
+        if (S > 1) {
+            // fp32 partial of this K split, summed (with the epilogue) by
+            // the split-K reduction kernel
+            float *ws = a.ws + static_cast<int64_t>(split) * M * N;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int64_t n = n0 + wn * TN + j * 16 + fr;
+                if (n >= N) continue;
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int64_t m = m0 + wm * TM + i * 16 + 4 * fg + v;
+                        if (m < M) __builtin_nontemporal_store(acc[i][j][v], ws + m * N + n);
+                    }
+            }
+        } else if (full) {
             lds_wait_all();
             barrier_nofence();
             uint16_t *stage0 = reinterpret_cast<uint16_t *>(lds + slot_add(s0, 3) * SLOT);
@@ -911,7 +947,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
         ca = na;
         cb = nb;
-        resources(tile + 2 * static_cast<int64_t>(gridDim.x), na, nb);
+        resources(item + 2 * static_cast<int64_t>(gridDim.x), na, nb, nkb);
     }
     // the copies issued for the tile after the last one (empty resource)
     // still write LDS: drain them before the workgroup ends
@@ -936,7 +972,7 @@ PROJ_GEMM_PP_VARIANTS(PROJ_GEMM_PP_INST)
 #define PROJ_GEMM_PP64_VARIANTS(X) X(256, 4) X(256, 8) X(192, 4)
 #define PROJ_GEMM_PP64_INST(BN, GM) template __global__ void gemm_pp64_kernel<BN, GM>(Args);
 PROJ_GEMM_PP64_VARIANTS(PROJ_GEMM_PP64_INST)
-#define PROJ_GEMM_PP64P_INST(BN, GM) template __global__ void gemm_pp64p_kernel<BN, GM>(Args);
+#define PROJ_GEMM_PP64P_INST(BN, GM) template __global__ void gemm_pp64p_kernel<BN, GM>(Args, int);
 PROJ_GEMM_PP64_VARIANTS(PROJ_GEMM_PP64P_INST)
 
 #ifndef __HIP_DEVICE_COMPILE__
@@ -951,7 +987,8 @@ static hipError_t prepare_gemm() {
 // prepare_gemm must have run once in the process (the library does it when a
 // context is created), so launching is capture-safe.
 template <int BM, int BN, int BK, int WM, int WN, int GM>
-static hipError_t launch_gemm(const Args &a, hipStream_t st) {
+static hipError_t launch_gemm(const Args &a, int S, hipStream_t st) {
+    if (S != 1) return hipErrorInvalidValue;
     const int64_t G = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
     if (G <= 0 || G > 0x7fffffff) return hipErrorInvalidConfiguration;
     constexpr int lds_bytes = 2 * (BM + BN) * BK * 2;
@@ -972,7 +1009,8 @@ static hipError_t prepare_gemm_pp() {
 }
 
 template <int BN, int GM>
-static hipError_t launch_gemm_pp(const Args &a, hipStream_t st) {
+static hipError_t launch_gemm_pp(const Args &a, int S, hipStream_t st) {
+    if (S != 1) return hipErrorInvalidValue;
     const int64_t G = ((a.M + 255) / 256) * ((a.N + BN - 1) / BN);
     if (G <= 0 || G > 0x7fffffff) return hipErrorInvalidConfiguration;
     constexpr int lds_bytes = 5 * (256 + BN) * 64;
@@ -988,7 +1026,8 @@ static hipError_t prepare_gemm_pp64() {
 }
 
 template <int BN, int GM>
-static hipError_t launch_gemm_pp64(const Args &a, hipStream_t st) {
+static hipError_t launch_gemm_pp64(const Args &a, int S, hipStream_t st) {
+    if (S != 1) return hipErrorInvalidValue;
     const int64_t G = ((a.M + 255) / 256) * ((a.N + BN - 1) / BN);
     if (G <= 0 || G > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((gemm_pp64_kernel<BN, GM>), dim3(static_cast<unsigned>(G)), dim3(512), 5 * 32 * 1024, st, a);
@@ -1010,26 +1049,31 @@ static hipError_t prepare_gemm_pp64p() {
                                5 * 32 * 1024);
 }
 
-// K < 128 (one k-range) runs the non-persistent kernel
+// K < 128 (one k-range) runs the non-persistent kernel; S > 1 splits K into
+// S parts of at least two k-ranges each and adds the reduction pass
 template <int BN, int GM>
-static hipError_t launch_gemm_pp64p(const Args &a, hipStream_t st) {
-    if (a.K < 128) return launch_gemm_pp64<BN, GM>(a, st);
-    const int64_t G = ((a.M + 255) / 256) * ((a.N + BN - 1) / BN);
+static hipError_t launch_gemm_pp64p(const Args &a, int S, hipStream_t st) {
+    if (a.K < 128) return S == 1 ? launch_gemm_pp64<BN, GM>(a, 1, st) : hipErrorInvalidValue;
+    if (S < 1 || a.K / 64 < 2 * static_cast<int64_t>(S)) return hipErrorInvalidValue;
+    const int64_t G = ((a.M + 255) / 256) * ((a.N + BN - 1) / BN) * S;
     if (G <= 0 || G > 0x7fffffff) return hipErrorInvalidConfiguration;
     const int64_t cus = g_num_cus > 0 ? g_num_cus : 256;
     const int64_t grid = G < cus ? G : cus;
-    hipLaunchKernelGGL((gemm_pp64p_kernel<BN, GM>), dim3(static_cast<unsigned>(grid)), dim3(512), 5 * 32 * 1024, st, a);
-    return hipGetLastError();
+    hipLaunchKernelGGL((gemm_pp64p_kernel<BN, GM>), dim3(static_cast<unsigned>(grid)), dim3(512), 5 * 32 * 1024, st, a,
+                       S);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || S == 1) return e;
+    return launch_splitk_reduce(a, S, st);
 }
 
 #define PROJ_GEMM_ENTRY(BM, BN, WM, WN, GM) \
-    {"gemm", BM, BN, 64, 64, WM, WN, GM, 0, &launch_gemm<BM, BN, 64, WM, WN, GM>, &prepare_gemm<BM, BN, 64, WM, WN, GM>},
+    {"gemm", BM, BN, 64, 64, WM, WN, GM, 0, 1, &launch_gemm<BM, BN, 64, WM, WN, GM>, &prepare_gemm<BM, BN, 64, WM, WN, GM>},
 #define PROJ_GEMM_PP_ENTRY(BN, GM) \
-    {"gemmpp", 256, BN, 32, 32, 4, 2, GM, kRingMaxK, &launch_gemm_pp<BN, GM>, &prepare_gemm_pp<BN, GM>},
+    {"gemmpp", 256, BN, 32, 32, 4, 2, GM, kRingMaxK, 1, &launch_gemm_pp<BN, GM>, &prepare_gemm_pp<BN, GM>},
 #define PROJ_GEMM_PP64_ENTRY(BN, GM) \
-    {"gemmpp64", 256, BN, 64, 64, 4, 2, GM, kRingMaxK, &launch_gemm_pp64<BN, GM>, &prepare_gemm_pp64<BN, GM>},
+    {"gemmpp64", 256, BN, 64, 64, 4, 2, GM, kRingMaxK, 1, &launch_gemm_pp64<BN, GM>, &prepare_gemm_pp64<BN, GM>},
 #define PROJ_GEMM_PP64P_ENTRY(BN, GM) \
-    {"gemmpp64p", 256, BN, 64, 64, 4, 2, GM, kRingMaxK, &launch_gemm_pp64p<BN, GM>, &prepare_gemm_pp64p<BN, GM>},
+    {"gemmpp64p", 256, BN, 64, 64, 4, 2, GM, kRingMaxK, 16, &launch_gemm_pp64p<BN, GM>, &prepare_gemm_pp64p<BN, GM>},
 const GemmVariant kGemmVariants[] = {PROJ_GEMM_VARIANTS(PROJ_GEMM_ENTRY) PROJ_GEMM_PP_VARIANTS(PROJ_GEMM_PP_ENTRY)
                                          PROJ_GEMM_PP64_VARIANTS(PROJ_GEMM_PP64_ENTRY)
                                              PROJ_GEMM_PP64_VARIANTS(PROJ_GEMM_PP64P_ENTRY)};

@@ -23,11 +23,16 @@ struct GemmVariant {
     const char *family;
     int bm, bn, bk, kmult, waves_m, waves_n, group_m;  // kmult: K must be a multiple of it
     int64_t kmax;  // largest K the kernel addresses (0: no limit)
-    hipError_t (*launch)(const Args &, hipStream_t);
+    int max_splits;  // largest K split count (1: the kernel does not split K)
+    hipError_t (*launch)(const Args &, int splits, hipStream_t);
     hipError_t (*prepare)();  // one-time function attributes (LDS size)
 };
 extern const GemmVariant kGemmVariants[];
 extern const int kNumGemmVariants;
+
+// Second pass of split-K (stream.hip): Y = epilogue(sum over the S fp32
+// partials in a.ws, in split order).
+hipError_t launch_splitk_reduce(const Args &a, int S, hipStream_t st);
 
 // Any shape, any alignment (generic.hip).
 hipError_t launch_generic(const Args &a, hipStream_t st);

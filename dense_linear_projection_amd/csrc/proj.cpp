@@ -131,10 +131,12 @@ std::string stream_name(const StreamVariant &v, int S) {
     return b;
 }
 
-std::string gemm_name(const GemmVariant &v) {
+std::string gemm_name(const GemmVariant &v, int S) {
     char b[96];
     snprintf(b, sizeof b, "%s_%dx%dx%d_w%dx%d_g%d", v.family, v.bm, v.bn, v.bk, v.waves_m, v.waves_n, v.group_m);
-    return b;
+    std::string n = b;
+    if (S > 1) n += "_s" + std::to_string(S);
+    return n;
 }
 
 // Every compiled variant that can run this shape correctly.  These are
@@ -162,7 +164,16 @@ std::vector<Candidate> candidates(const Key &k) {
             const GemmVariant &v = kGemmVariants[i];
             if (k.K % v.kmult != 0) continue;
             if (v.kmax > 0 && k.K > v.kmax) continue;
-            out.push_back({KIND_GEMM, i, 1, gemm_name(v)});
+            out.push_back({KIND_GEMM, i, 1, gemm_name(v, 1)});
+            // K splits: at least two 64-wide k-ranges each, partials fit the
+            // workspace, and split only while the tiles alone leave CUs idle
+            const int64_t tiles = ((k.M + v.bm - 1) / v.bm) * ((k.N + v.bn - 1) / v.bn);
+            for (int S = 2; S <= v.max_splits; S *= 2) {
+                if (k.K / 64 < 2 * static_cast<int64_t>(S)) break;
+                if (static_cast<size_t>(S) * k.M * k.N * sizeof(float) > kWorkspaceBytes) break;
+                if (tiles * (S / 2) >= 256) break;
+                out.push_back({KIND_GEMM, i, S, gemm_name(v, S)});
+            }
         }
     }
     if (out.empty()) out.push_back({KIND_GENERIC, 0, 1, "generic"});
@@ -217,7 +228,7 @@ Args make_args(proj_ctx *c, const void *X, const void *W, const void *bias, int 
 
 hipError_t launch(const Candidate &cand, const Args &a, hipStream_t st) {
     switch (cand.kind) {
-        case KIND_GEMM: return kGemmVariants[cand.variant].launch(a, st);
+        case KIND_GEMM: return kGemmVariants[cand.variant].launch(a, cand.splits, st);
         case KIND_STREAM: return kStreamVariants[cand.variant].launch(a, cand.splits, st);
         default: return launch_generic(a, st);
     }

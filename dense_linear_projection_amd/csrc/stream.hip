@@ -314,7 +314,12 @@ static hipError_t launch_stream(const Args &a, int S, hipStream_t st) {
                            dim3(WV * 64), lds_bytes, st, a, S);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || S == 1) return e;
+    return launch_splitk_reduce(a, S, st);
+}
+
+hipError_t launch_splitk_reduce(const Args &a, int S, hipStream_t st) {
     const int64_t blocks = (a.M * a.N + 255) / 256;
+    if (blocks <= 0 || blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a, S);
     return hipGetLastError();
 }

@@ -114,6 +114,39 @@ def test_persistent_tile_walk(ctx):
         assert rep["ok"], "%s: %s" % (name, rep)
 
 
+def test_split_k_item_walk(ctx):
+    """K-split candidates with more (tile, split) items than CUs, so
+    persistent workgroups walk several items whose k-ranges differ; ragged
+    last tile row and column.  Integer inputs: bit-exact (partials and their
+    reduction are exact); then GELU with random inputs within tolerance."""
+    # 3 x 31 tiles of 256 x 256 (ragged), 4 splits: 372 items; four fp32
+    # partials fit the 64 MiB workspace
+    M, N, K = 520, 7700, 512
+    X = synth.integer_bf16((M, K), -8, 8, 51)
+    W = synth.integer_bf16((N, K), -8, 8, 52)
+    b = synth.integer_bf16((N,), -64, 64, 53)
+    Xd, Wd, bd = dev_bf16(X), dev_bf16(W), dev_bf16(b)
+    for epi, out in ((oracle.EPI_BIAS, oracle.OUT_BF16), (oracle.EPI_NONE, oracle.OUT_F32)):
+        r, _ = oracle.reference(X, W, b if epi & 1 else None, epi, out)
+        names = candidate_names(M, N, K, epi, out)
+        split = [(i, n) for i, n in enumerate(names) if "_s" in n and n.startswith("gemm")]
+        assert any(n.endswith("_s4") for _, n in split)
+        for i, name in split:
+            u = run_candidate(ctx, i, Xd, Wd, bd, epi, M, N, K, out)
+            bad = np.argwhere(u != r)
+            assert bad.size == 0, "%s epi=%d out=%d: %d mismatches, first at %s: %r vs %r" % (
+                name, epi, out, len(bad), bad[0], u[tuple(bad[0])], r[tuple(bad[0])])
+    Xr, Wr, br = synth.make_inputs(M, N, K, True, 54)
+    Xd, Wd, bd = dev_bf16(Xr), dev_bf16(Wr), dev_bf16(br)
+    r, _ = oracle.reference(Xr, Wr, br, oracle.EPI_BIAS_GELU, oracle.OUT_BF16)
+    for i, name in enumerate(candidate_names(M, N, K, oracle.EPI_BIAS_GELU, oracle.OUT_BF16)):
+        if "_s" not in name or not name.startswith("gemm"):
+            continue
+        u = run_candidate(ctx, i, Xd, Wd, bd, oracle.EPI_BIAS_GELU, M, N, K, oracle.OUT_BF16)
+        rep = compare.check(u, r)
+        assert rep["ok"], "%s: %s" % (name, rep)
+
+
 @pytest.mark.parametrize("M", [1, 15, 16, 17, 63, 64, 65, 127, 128, 129])
 def test_token_counts_around_tile_edges(ctx, M):
     """Tuned plan (proj_run) at token counts on both sides of tile edges."""
