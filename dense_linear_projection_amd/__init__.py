@@ -10,7 +10,10 @@ binding's entry points raises.
 Names mirror the C ABI: ``proj_create``, ``proj_run``, ``proj_destroy``,
 ``proj_tune``, ``proj_get_plan``, ``proj_num_candidates``,
 ``proj_candidate_name``, ``proj_run_candidate``, ``proj_graph_capture``,
-``proj_graph_launch``, ``proj_graph_destroy``, ``proj_status_string``.
+``proj_graph_launch``, ``proj_graph_destroy``, ``proj_status_string``, and
+for fp32 weights held as a bf16 high/low pair ``proj_prepare_hilo``,
+``proj_run_hilo``, ``proj_get_plan_hilo``, ``proj_num_candidates_hilo``,
+``proj_candidate_name_hilo``, ``proj_run_candidate_hilo``.
 """
 from __future__ import annotations
 
@@ -33,7 +36,9 @@ OUT_F32, OUT_BF16 = 0, 1
 
 EXPORTS = ["proj_create", "proj_run", "proj_tune", "proj_destroy", "proj_status_string",
            "proj_last_error", "proj_get_plan", "proj_num_candidates", "proj_candidate_name",
-           "proj_run_candidate", "proj_graph_capture", "proj_graph_launch", "proj_graph_destroy"]
+           "proj_run_candidate", "proj_graph_capture", "proj_graph_launch", "proj_graph_destroy",
+           "proj_prepare_hilo", "proj_run_hilo", "proj_get_plan_hilo", "proj_num_candidates_hilo",
+           "proj_candidate_name_hilo", "proj_run_candidate_hilo"]
 
 
 class ProjError(RuntimeError):
@@ -72,6 +77,12 @@ def lib() -> ctypes.CDLL:
                                 ctypes.POINTER(vp), ci, i64, i64, i64, ci, vp, ctypes.POINTER(vp)], st),
         "proj_graph_launch": ([vp, vp], st),
         "proj_graph_destroy": ([vp], st),
+        "proj_prepare_hilo": ([vp, vp, i64, i64, vp, vp], st),
+        "proj_run_hilo": (run_args, st),
+        "proj_get_plan_hilo": ([vp, i64, i64, i64, ci, ci, ci, ctypes.c_char_p, ctypes.c_size_t], st),
+        "proj_num_candidates_hilo": ([i64, i64, i64, ci, ci, ci], ci),
+        "proj_candidate_name_hilo": ([i64, i64, i64, ci, ci, ci, ci, ctypes.c_char_p, ctypes.c_size_t], st),
+        "proj_run_candidate_hilo": ([vp, ci, vp, vp, vp, ci, i64, i64, i64, vp, ci, vp], st),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -210,6 +221,69 @@ def proj_run_candidate(ctx, index, X, W, bias, epilogue, Y, M=None, N=None, K=No
     M, N, K = _shape(X, W, M, N, K)
     _check(lib().proj_run_candidate(ctx, int(index), _ptr(X), _ptr(W), _ptr(bias), int(epilogue), M, N, K,
                                     _ptr(Y), _out_dtype(Y, out_dtype), _stream(stream)), ctx)
+
+
+# ---------------------------------------------- fp32 weights, high/low pair
+
+def proj_prepare_hilo(ctx, W, Whl=None, stream=None):
+    """Register fp32 weights W [N, K] (device float32 tensor) as the bf16
+    pair Whl [N, 2K] = [H | L] (allocated here if not given); returns Whl."""
+    import torch
+    if W.dtype != torch.float32 or W.dim() != 2:
+        raise ValueError("W must be a float32 [N, K] tensor")
+    N, K = W.shape
+    if Whl is None:
+        Whl = torch.empty((N, 2 * K), dtype=torch.bfloat16, device=W.device)
+    elif Whl.dtype != torch.bfloat16 or tuple(Whl.shape) != (N, 2 * K):
+        raise ValueError("Whl must be bfloat16 [N, 2K]")
+    _check(lib().proj_prepare_hilo(ctx, _ptr(W), int(N), int(K), _ptr(Whl), _stream(stream)), ctx)
+    return Whl
+
+
+def _shape_hilo(X, Whl, M, N, K):
+    if M is None:
+        M = X.shape[0]
+    if N is None:
+        N = Whl.shape[0]
+    if K is None:
+        K = X.shape[1]
+    return int(M), int(N), int(K)
+
+
+def proj_run_hilo(ctx, X, Whl, bias, epilogue, Y, M=None, N=None, K=None, out_dtype=None, stream=None) -> None:
+    """Enqueue Y = epilogue(X . H^T + X . L^T [+ bias]) for X bf16 [M, K] and
+    a registered pair Whl bf16 [N, 2K]."""
+    _check_operands(X, Whl, bias, Y)
+    M, N, K = _shape_hilo(X, Whl, M, N, K)
+    _check(lib().proj_run_hilo(ctx, _ptr(X), _ptr(Whl), _ptr(bias), int(epilogue), M, N, K, _ptr(Y),
+                               _out_dtype(Y, out_dtype), _stream(stream)), ctx)
+
+
+def proj_get_plan_hilo(ctx, M, N, K, epilogue, out_dtype, aligned16=True) -> str:
+    buf = ctypes.create_string_buffer(256)
+    _check(lib().proj_get_plan_hilo(ctx, int(M), int(N), int(K), int(epilogue), int(out_dtype),
+                                    1 if aligned16 else 0, buf, 256), ctx)
+    return buf.value.decode()
+
+
+def proj_num_candidates_hilo(M, N, K, epilogue, out_dtype, aligned16=True) -> int:
+    return int(lib().proj_num_candidates_hilo(int(M), int(N), int(K), int(epilogue), int(out_dtype),
+                                              1 if aligned16 else 0))
+
+
+def proj_candidate_name_hilo(M, N, K, epilogue, out_dtype, index, aligned16=True) -> str:
+    buf = ctypes.create_string_buffer(256)
+    _check(lib().proj_candidate_name_hilo(int(M), int(N), int(K), int(epilogue), int(out_dtype),
+                                          1 if aligned16 else 0, int(index), buf, 256))
+    return buf.value.decode()
+
+
+def proj_run_candidate_hilo(ctx, index, X, Whl, bias, epilogue, Y, M=None, N=None, K=None, out_dtype=None,
+                            stream=None) -> None:
+    _check_operands(X, Whl, bias, Y)
+    M, N, K = _shape_hilo(X, Whl, M, N, K)
+    _check(lib().proj_run_candidate_hilo(ctx, int(index), _ptr(X), _ptr(Whl), _ptr(bias), int(epilogue), M, N, K,
+                                         _ptr(Y), _out_dtype(Y, out_dtype), _stream(stream)), ctx)
 
 
 def proj_graph_capture(ctx, Xs, Ws, biases, Ys, epilogue, out_dtype=None, stream=None) -> int:

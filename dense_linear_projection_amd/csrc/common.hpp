@@ -22,6 +22,7 @@ struct Args {
     const uint16_t *bias;  // bf16 [N] or nullptr
     void *Y;               // fp32 / bf16 [M, N]
     int64_t M, N, K;
+    int64_t kx;            // X row length: K, or K/2 for a hi/lo weight pair (X column k' reads k' mod kx)
     int epi, out;
     float *ws;             // split-K partials [S][M][N] (library-owned)
     const uint16_t *zeros; // >= 64 zero bytes in device memory, for masked loads

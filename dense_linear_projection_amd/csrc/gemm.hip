@@ -759,18 +759,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         origin(item, m0, n0);
         const int64_t rows_a = (M - m0) < BM ? (M - m0) : BM;
         const int64_t rows_b = (N - n0) < BN ? (N - n0) : BN;
-        ra = buffer_rsrc(a.X + m0 * K, static_cast<uint32_t>(rows_a * K * 2));
+        ra = buffer_rsrc(a.X + m0 * a.kx, static_cast<uint32_t>(rows_a * a.kx * 2));
         rb = buffer_rsrc(a.W + n0 * K, static_cast<uint32_t>(rows_b * K * 2));
     };
 
     const int drow = lane >> 3;
+    // X rows are kx long (K, or K/2 for a hi/lo weight pair, whose second
+    // half of k-ranges reads X from the start again)
+    const int KHX = static_cast<int>(a.kx / 64);
     auto copy_a = [&](__amdgpu_buffer_rsrc_t r, int T, int slot) {
-        const uint32_t soff = static_cast<uint32_t>(T * ROWB);
+        const uint32_t soff = static_cast<uint32_t>((T >= KHX ? T - KHX : T) * ROWB);
 #pragma unroll
         for (int j = 0; j < NCA; ++j) {
             const int b = grp * (A_BLK / 2) + wg + 4 * j;
             const int row = b * 8 + drow;
-            dma16_buf(r, static_cast<uint32_t>(row * K * 2 + ((lane & 7) ^ swz128(row)) * 16), soff,
+            dma16_buf(r, static_cast<uint32_t>(row * a.kx * 2 + ((lane & 7) ^ swz128(row)) * 16), soff,
                       lds + slot * SLOT + b * 1024);
         }
     };
@@ -988,7 +991,7 @@ static hipError_t prepare_gemm() {
 // context is created), so launching is capture-safe.
 template <int BM, int BN, int BK, int WM, int WN, int GM>
 static hipError_t launch_gemm(const Args &a, int S, hipStream_t st) {
-    if (S != 1) return hipErrorInvalidValue;
+    if (S != 1 || a.kx != a.K) return hipErrorInvalidValue;  // no K split, no hi/lo pair
     const int64_t G = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
     if (G <= 0 || G > 0x7fffffff) return hipErrorInvalidConfiguration;
     constexpr int lds_bytes = 2 * (BM + BN) * BK * 2;
@@ -1010,7 +1013,7 @@ static hipError_t prepare_gemm_pp() {
 
 template <int BN, int GM>
 static hipError_t launch_gemm_pp(const Args &a, int S, hipStream_t st) {
-    if (S != 1) return hipErrorInvalidValue;
+    if (S != 1 || a.kx != a.K) return hipErrorInvalidValue;  // no K split, no hi/lo pair
     const int64_t G = ((a.M + 255) / 256) * ((a.N + BN - 1) / BN);
     if (G <= 0 || G > 0x7fffffff) return hipErrorInvalidConfiguration;
     constexpr int lds_bytes = 5 * (256 + BN) * 64;
@@ -1027,7 +1030,7 @@ static hipError_t prepare_gemm_pp64() {
 
 template <int BN, int GM>
 static hipError_t launch_gemm_pp64(const Args &a, int S, hipStream_t st) {
-    if (S != 1) return hipErrorInvalidValue;
+    if (S != 1 || a.kx != a.K) return hipErrorInvalidValue;  // no K split, no hi/lo pair
     const int64_t G = ((a.M + 255) / 256) * ((a.N + BN - 1) / BN);
     if (G <= 0 || G > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((gemm_pp64_kernel<BN, GM>), dim3(static_cast<unsigned>(G)), dim3(512), 5 * 32 * 1024, st, a);
@@ -1053,6 +1056,7 @@ static hipError_t prepare_gemm_pp64p() {
 // S parts of at least two k-ranges each and adds the reduction pass
 template <int BN, int GM>
 static hipError_t launch_gemm_pp64p(const Args &a, int S, hipStream_t st) {
+    if (a.kx != a.K && (a.kx % 64 != 0 || a.K < 128)) return hipErrorInvalidValue;
     if (a.K < 128) return S == 1 ? launch_gemm_pp64<BN, GM>(a, 1, st) : hipErrorInvalidValue;
     if (S < 1 || a.K / 64 < 2 * static_cast<int64_t>(S)) return hipErrorInvalidValue;
     const int64_t G = ((a.M + 255) / 256) * ((a.N + BN - 1) / BN) * S;

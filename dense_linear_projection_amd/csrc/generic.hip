@@ -16,12 +16,30 @@ __global__ __launch_bounds__(256) void generic_kernel(Args a) {
     const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     if (idx >= a.M * a.N) return;
     const int64_t m = idx / a.N, n = idx % a.N;
-    const uint16_t *x = a.X + m * a.K;
+    const uint16_t *x = a.X + m * a.kx;
     const uint16_t *w = a.W + n * a.K;
     float s = 0.f;
-    for (int64_t k = 0; k < a.K; ++k) s = __builtin_fmaf(bf16_bits_to_f32(x[k]), bf16_bits_to_f32(w[k]), s);
+    for (int64_t k = 0; k < a.K; ++k)
+        s = __builtin_fmaf(bf16_bits_to_f32(x[k < a.kx ? k : k - a.kx]), bf16_bits_to_f32(w[k]), s);
     const float b = (a.epi & 1) ? bf16_bits_to_f32(a.bias[n]) : 0.f;
     store_out(a.Y, a.out, idx, apply_epilogue(s, a.epi, b));
+}
+
+// Weight registration for fp32 weights (worklog, section "Why the high-plus-
+// low router scheme helped"): H = bf16(W), R = W - fp32(H) (exact in fp32:
+// R is W's part below H's last bit), L = bf16(R), both with round to
+// nearest even, stored per row as [H(n, 0..K-1), L(n, 0..K-1)], so that
+// X W^T ~ X H^T + X L^T is one projection of depth 2K whose X columns wrap
+// at K.  Non-finite weights pass through H (their L is NaN or zero).
+__global__ __launch_bounds__(256) void hilo_split_kernel(const float *W, int64_t N, int64_t K, uint16_t *out) {
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (idx >= N * K) return;
+    const int64_t n = idx / K, k = idx % K;
+    const float w = W[idx];
+    const uint16_t h = f32_to_bf16_bits(w);
+    const uint16_t l = f32_to_bf16_bits(w - bf16_bits_to_f32(h));
+    out[n * 2 * K + k] = h;
+    out[n * 2 * K + K + k] = l;
 }
 
 // Reads a large buffer so that the caches hold clean lines of it instead of
@@ -41,6 +59,13 @@ __global__ __launch_bounds__(256) void flush_read_kernel(const u32x4 *p, int64_t
 hipError_t launch_flush(const void *buf, size_t bytes, unsigned *sink, hipStream_t st) {
     hipLaunchKernelGGL(flush_read_kernel, dim3(2048), dim3(256), 0, st, static_cast<const u32x4 *>(buf),
                        static_cast<int64_t>(bytes / 16), sink);
+    return hipGetLastError();
+}
+
+hipError_t launch_hilo_split(const float *W, int64_t N, int64_t K, uint16_t *out, hipStream_t st) {
+    const int64_t blocks = (N * K + 255) / 256;
+    if (blocks <= 0 || blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(hilo_split_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, W, N, K, out);
     return hipGetLastError();
 }
 

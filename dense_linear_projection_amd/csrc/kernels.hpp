@@ -37,6 +37,9 @@ hipError_t launch_splitk_reduce(const Args &a, int S, hipStream_t st);
 // Any shape, any alignment (generic.hip).
 hipError_t launch_generic(const Args &a, hipStream_t st);
 
+// fp32 weights [N][K] -> bf16 hi/lo pair [N][2K] (generic.hip).
+hipError_t launch_hilo_split(const float *W, int64_t N, int64_t K, uint16_t *out, hipStream_t st);
+
 // Read `bytes` of `buf` to evict other data from the caches (generic.hip);
 // `sink` needs room for 256 unsigned.
 hipError_t launch_flush(const void *buf, size_t bytes, unsigned *sink, hipStream_t st);

@@ -38,11 +38,14 @@ constexpr size_t kWorkspaceBytes = 64ull << 20;
 constexpr size_t kZeroBytes = 256;
 constexpr size_t kFlushBytes = 512ull << 20;  // larger than the last-level cache
 
+// K is the depth of the product: for a hi/lo weight pair (hilo = 1) twice
+// the X row length
 struct Key {
     int64_t M, N, K;
     int epi, out, aligned;
+    int hilo = 0;
     bool operator<(const Key &o) const {
-        return std::tie(M, N, K, epi, out, aligned) < std::tie(o.M, o.N, o.K, o.epi, o.out, o.aligned);
+        return std::tie(M, N, K, epi, out, aligned, hilo) < std::tie(o.M, o.N, o.K, o.epi, o.out, o.aligned, o.hilo);
     }
 };
 
@@ -150,6 +153,13 @@ std::vector<Candidate> candidates(const Key &k) {
             for (int i = 0; i < kNumStreamVariants; ++i) {
                 const StreamVariant &v = kStreamVariants[i];
                 if (v.mt != mt) continue;
+                // a hi/lo pair is read on the buffer-resource path only: whole
+                // stages, the X wrap at K/2 on a stage boundary, and operand
+                // offsets that fit its 32-bit resources
+                if (k.hilo && (k.K % v.kc != 0 || (k.K / 2) % v.kc != 0 ||
+                               k.M * (k.K / 2) * 2 >= (int64_t{1} << 32) ||
+                               int64_t{16} * v.nt * k.K * 2 >= (int64_t{1} << 32)))
+                    continue;
                 const int64_t stages = (k.K + v.kc - 1) / v.kc;
                 const int64_t tiles = (k.N + 16 * v.nt - 1) / (16 * v.nt);
                 for (int S : {1, 2, 4, 8}) {
@@ -163,6 +173,8 @@ std::vector<Candidate> candidates(const Key &k) {
         for (int i = 0; i < kNumGemmVariants; ++i) {
             const GemmVariant &v = kGemmVariants[i];
             if (k.K % v.kmult != 0) continue;
+            // the persistent kernel is the GEMM that reads a hi/lo pair
+            if (k.hilo && (std::strcmp(v.family, "gemmpp64p") != 0 || (k.K / 2) % 64 != 0 || k.K < 128)) continue;
             if (v.kmax > 0 && k.K > v.kmax) continue;
             out.push_back({KIND_GEMM, i, 1, gemm_name(v, 1)});
             // K splits: at least two 64-wide k-ranges each, partials fit the
@@ -210,8 +222,9 @@ Candidate default_candidate(const Key &k) {
 }
 
 Args make_args(proj_ctx *c, const void *X, const void *W, const void *bias, int epi, int64_t M, int64_t N,
-               int64_t K, void *Y, int out) {
+               int64_t K, void *Y, int out, int hilo = 0) {
     Args a;
+    a.kx = hilo ? K / 2 : K;
     a.X = static_cast<const uint16_t *>(X);
     a.W = static_cast<const uint16_t *>(W);
     a.bias = static_cast<const uint16_t *>(bias);
@@ -277,10 +290,10 @@ proj_status check_args(proj_ctx *c, const void *X, const void *W, const void *bi
     return PROJ_OK;
 }
 
-Key make_key(const void *X, const void *W, int epi, int64_t M, int64_t N, int64_t K, int out) {
+Key make_key(const void *X, const void *W, int epi, int64_t M, int64_t N, int64_t K, int out, int hilo = 0) {
     const bool al = (reinterpret_cast<uintptr_t>(X) % 16 == 0) && (reinterpret_cast<uintptr_t>(W) % 16 == 0) &&
-                    (K % 8 == 0);
-    return Key{M, N, K, epi, out, al ? 1 : 0};
+                    ((hilo ? K / 2 : K) % 8 == 0);
+    return Key{M, N, K, epi, out, al ? 1 : 0, hilo};
 }
 
 bool capturing(hipStream_t st) {
@@ -379,13 +392,13 @@ proj_status tune(proj_ctx *c, const Key &k, const Args &a, hipStream_t st, Plan 
 }
 
 proj_status run_impl(proj_ctx *c, const void *X, const void *W, const void *bias, int epi, int64_t M, int64_t N,
-                     int64_t K, void *Y, int out, void *stream, bool force_tune) {
+                     int64_t K, void *Y, int out, void *stream, bool force_tune, int hilo = 0) {
     proj_status s = check_args(c, X, W, bias, epi, M, N, K, Y, out);
     if (s != PROJ_OK || M == 0 || N == 0) return s;
     DeviceGuard g(c->device);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const Key k = make_key(X, W, epi, M, N, K, out);
-    const Args a = make_args(c, X, W, bias, epi, M, N, K, Y, out);
+    const Key k = make_key(X, W, epi, M, N, K, out, hilo);
+    const Args a = make_args(c, X, W, bias, epi, M, N, K, Y, out, hilo);
     const bool cap = capturing(st);
     if (force_tune && cap) {
         set_err(c, "cannot tune while the stream is capturing");
@@ -458,6 +471,31 @@ proj_status proj_tune(proj_ctx *ctx, const void *X, const void *W, const void *b
     return run_impl(ctx, X, W, bias, epilogue, M, N, K, Y, out_dtype, stream, true);
 }
 
+proj_status proj_prepare_hilo(proj_ctx *ctx, const float *W, int64_t N, int64_t K, void *Whl, void *stream) {
+    if (!ctx) return PROJ_ERR_INVALID_ARG;
+    if (ctx->magic == kDead) return PROJ_ERR_DESTROYED;
+    if (ctx->magic != kMagic) return PROJ_ERR_INVALID_ARG;
+    if (N < 0 || K < 0) {
+        set_err(ctx, "negative size N=%lld K=%lld", (long long)N, (long long)K);
+        return PROJ_ERR_INVALID_ARG;
+    }
+    if (N == 0 || K == 0) return PROJ_OK;
+    if (!W || !Whl || reinterpret_cast<uintptr_t>(W) % 4 || reinterpret_cast<uintptr_t>(Whl) % 2) {
+        set_err(ctx, "W or Whl is NULL or not aligned to its element size");
+        return PROJ_ERR_INVALID_ARG;
+    }
+    DeviceGuard g(ctx->device);
+    hipError_t e = launch_hilo_split(W, N, K, static_cast<uint16_t *>(Whl), static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(ctx, "launch", e);
+    return PROJ_OK;
+}
+
+proj_status proj_run_hilo(proj_ctx *ctx, const void *X, const void *Whl, const void *bias, int epilogue, int64_t M,
+                          int64_t N, int64_t K, void *Y, int out_dtype, void *stream) {
+    if (K < 0 || K > (int64_t(1) << 40)) return PROJ_ERR_INVALID_ARG;
+    return run_impl(ctx, X, Whl, bias, epilogue, M, N, 2 * K, Y, out_dtype, stream, false, 1);
+}
+
 proj_status proj_destroy(proj_ctx *ctx) {
     if (!ctx) return PROJ_ERR_INVALID_ARG;
     if (ctx->magic == kDead) return PROJ_ERR_DESTROYED;
@@ -492,11 +530,10 @@ const char *proj_last_error(const proj_ctx *ctx) {
     return ctx->err.c_str();
 }
 
-proj_status proj_get_plan(proj_ctx *ctx, int64_t M, int64_t N, int64_t K, int epi, int out, int aligned16,
-                          char *buf, size_t len) {
+static proj_status get_plan(proj_ctx *ctx, const Key &key, char *buf, size_t len) {
     if (!ctx || ctx->magic != kMagic || !buf || len == 0) return PROJ_ERR_INVALID_ARG;
     std::lock_guard<std::mutex> lock(ctx->mu);
-    auto it = ctx->plans.find(Key{M, N, K, epi, out, aligned16 ? 1 : 0});
+    auto it = ctx->plans.find(key);
     if (it == ctx->plans.end()) return PROJ_ERR_INVALID_ARG;
     char tmp[256];
     if (it->second.tuned)
@@ -508,9 +545,51 @@ proj_status proj_get_plan(proj_ctx *ctx, int64_t M, int64_t N, int64_t K, int ep
     return PROJ_OK;
 }
 
+proj_status proj_get_plan(proj_ctx *ctx, int64_t M, int64_t N, int64_t K, int epi, int out, int aligned16,
+                          char *buf, size_t len) {
+    return get_plan(ctx, Key{M, N, K, epi, out, aligned16 ? 1 : 0}, buf, len);
+}
+
+proj_status proj_get_plan_hilo(proj_ctx *ctx, int64_t M, int64_t N, int64_t K, int epi, int out, int aligned16,
+                               char *buf, size_t len) {
+    return get_plan(ctx, Key{M, N, 2 * K, epi, out, aligned16 ? 1 : 0, 1}, buf, len);
+}
+
 int proj_num_candidates(int64_t M, int64_t N, int64_t K, int epi, int out, int aligned16) {
     if (M <= 0 || N <= 0 || K < 0) return 0;
     return static_cast<int>(candidates(Key{M, N, K, epi, out, aligned16 ? 1 : 0}).size());
+}
+
+int proj_num_candidates_hilo(int64_t M, int64_t N, int64_t K, int epi, int out, int aligned16) {
+    if (M <= 0 || N <= 0 || K < 0) return 0;
+    return static_cast<int>(candidates(Key{M, N, 2 * K, epi, out, aligned16 ? 1 : 0, 1}).size());
+}
+
+proj_status proj_candidate_name_hilo(int64_t M, int64_t N, int64_t K, int epi, int out, int aligned16, int index,
+                                     char *buf, size_t len) {
+    if (M <= 0 || N <= 0 || K < 0 || !buf) return PROJ_ERR_INVALID_ARG;
+    std::vector<Candidate> c = candidates(Key{M, N, 2 * K, epi, out, aligned16 ? 1 : 0, 1});
+    if (index < 0 || index >= static_cast<int>(c.size())) return PROJ_ERR_INVALID_ARG;
+    if (c[index].name.size() + 1 > len) return PROJ_ERR_INVALID_ARG;
+    std::strcpy(buf, c[index].name.c_str());
+    return PROJ_OK;
+}
+
+proj_status proj_run_candidate_hilo(proj_ctx *ctx, int index, const void *X, const void *Whl, const void *bias,
+                                    int epi, int64_t M, int64_t N, int64_t K, void *Y, int out, void *stream) {
+    proj_status s = check_args(ctx, X, Whl, bias, epi, M, N, 2 * K, Y, out);
+    if (s != PROJ_OK || M == 0 || N == 0) return s;
+    const Key k = make_key(X, Whl, epi, M, N, 2 * K, out, 1);
+    std::vector<Candidate> c = candidates(k);
+    if (index < 0 || index >= static_cast<int>(c.size())) {
+        set_err(ctx, "candidate %d out of range (%d)", index, static_cast<int>(c.size()));
+        return PROJ_ERR_INVALID_ARG;
+    }
+    DeviceGuard g(ctx->device);
+    hipError_t e = launch(c[index], make_args(ctx, X, Whl, bias, epi, M, N, 2 * K, Y, out, 1),
+                          static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(ctx, "launch", e);
+    return PROJ_OK;
 }
 
 proj_status proj_candidate_name(int64_t M, int64_t N, int64_t K, int epi, int out, int aligned16, int index,

@@ -135,20 +135,23 @@ __global__ __launch_bounds__(WAVES * 64) void stream_kernel(Args a, int S) {
     if constexpr (FAST) {
         const int64_t rows_w = (N - n0) < C::NR ? (N - n0) : C::NR;
         wbytes = static_cast<uint32_t>(rows_w * K * 2);
-        xbytes = static_cast<uint32_t>(M * K * 2);
+        xbytes = static_cast<uint32_t>(M * a.kx * 2);
 #pragma unroll
         for (int j = 0; j < C::PERW; ++j) {
             const int row = (wave + j * WAVES) * C::RPI + lane / C::CPR;
             const int chunk = (lane % C::CPR) ^ (row & 15);
-            const int64_t r = row < C::NR ? row : row - C::NR;
-            voff[j] = static_cast<uint32_t>((r * K + chunk * 8) * 2);
+            // W rows are K long, X rows kx long
+            voff[j] = static_cast<uint32_t>(row < C::NR ? (row * K + chunk * 8) * 2 : ((row - C::NR) * a.kx + chunk * 8) * 2);
         }
     }
     auto issue = [&](int i) {
         char *slot = lds + (i % D) * C::STAGE;
         if constexpr (FAST) {
             const bool live = i < nst;
-            const uint32_t soff = static_cast<uint32_t>(stage_k0(live ? i : 0) * 2);
+            const int64_t k0 = stage_k0(live ? i : 0);
+            const uint32_t soff = static_cast<uint32_t>(k0 * 2);
+            // X column of a hi/lo pair's second half wraps to the start
+            const uint32_t soffx = static_cast<uint32_t>((k0 >= a.kx ? k0 - a.kx : k0) * 2);
             const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(a.W + n0 * K, live ? wbytes : 0u);
             const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(a.X, live ? xbytes : 0u);
 #pragma unroll
@@ -159,7 +162,7 @@ __global__ __launch_bounds__(WAVES * 64) void stream_kernel(Args a, int S) {
                 if (WNT && is_w)
                     dma16_buf_nt(r, voff[j], soff, to);
                 else
-                    dma16_buf(r, voff[j], soff, to);
+                    dma16_buf(r, voff[j], is_w ? soff : soffx, to);
             }
         } else {
             const int64_t k0 = i < nst ? stage_k0(i) : 0;
@@ -304,8 +307,12 @@ static hipError_t launch_stream(const Args &a, int S, hipStream_t st) {
     const int64_t grid = tiles * S;
     if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     constexpr int lds_bytes = StreamCfg<MT, NT, WV, KC, D>::LDS;
-    // the buffer-resource path needs whole stages and 32-bit operand offsets
-    const bool fast = a.K % KC == 0 && a.M * a.K * 2 < (int64_t{1} << 32) && 16 * NT * a.K * 2 < (int64_t{1} << 32);
+    // the buffer-resource path needs whole stages and 32-bit operand offsets;
+    // it is also the only one that reads a hi/lo pair's X (kx < K), whose
+    // wrap must fall on a stage boundary
+    const bool fast = a.K % KC == 0 && a.kx % KC == 0 && a.M * a.kx * 2 < (int64_t{1} << 32) &&
+                      16 * NT * a.K * 2 < (int64_t{1} << 32);
+    if (!fast && a.kx != a.K) return hipErrorInvalidValue;
     if (fast)
         hipLaunchKernelGGL((stream_kernel<MT, NT, WV, KC, D, WNT, true>), dim3(static_cast<unsigned>(grid)),
                            dim3(WV * 64), lds_bytes, st, a, S);

@@ -116,6 +116,32 @@ proj_status proj_tune(proj_ctx *ctx, const void *X, const void *W, const void *b
                       int epilogue, int64_t M, int64_t N, int64_t K, void *Y,
                       int out_dtype, void *stream);
 
+/* ---- fp32 weights as a bf16 high/low pair (worklog "How I made Muse's GPU
+ * projections 1.32x faster in the Open Kernel Challenge", section "Why the
+ * high-plus-low router scheme helped"; the router's weights are fp32 in the
+ * section "The same calculation shows up in different sizes").
+ *
+ * Registration: for fp32 W [N][K] (device, row-major), writes Whl, a
+ * caller-allocated device array of bf16 [N][2K], row n = [H(n, 0..K-1),
+ * L(n, 0..K-1)] with H = bf16(W), L = bf16(W - fp32(H)), both rounded to
+ * nearest even.  Enqueued on `stream`; W and Whl stay owned by the caller.
+ * N = 0 or K = 0 is a no-op; NULL or misaligned pointers (W to 4, Whl to 2
+ * bytes) and negative sizes give PROJ_ERR_INVALID_ARG. */
+proj_status proj_prepare_hilo(proj_ctx *ctx, const float *W, int64_t N, int64_t K, void *Whl,
+                              void *stream);
+
+/* Y = epilogue(X H^T + X L^T (+ bias)) for X bf16 [M][K] and a registered
+ * pair Whl bf16 [N][2K]: one product of depth 2K, fp32 accumulation, whose X
+ * columns wrap at K (the high and the low part meet the same X values).
+ * Arguments, output and capture rules as proj_run, with K the X row length.
+ * The plan is measured per shape as for proj_run, among the kernels that
+ * read a wrapped X (the weight-streaming kernel's buffer-resource path when
+ * K is a multiple of its stage depth, the persistent GEMM when K is a
+ * multiple of 64), with the any-shape kernel as the fallback. */
+proj_status proj_run_hilo(proj_ctx *ctx, const void *X, const void *Whl, const void *bias,
+                          int epilogue, int64_t M, int64_t N, int64_t K, void *Y,
+                          int out_dtype, void *stream);
+
 /* Free the context (synchronises its device first).  The handle must not be
  * used afterwards; a second destroy of the same pointer is undefined. */
 proj_status proj_destroy(proj_ctx *ctx);
@@ -148,6 +174,19 @@ proj_status proj_candidate_name(int64_t M, int64_t N, int64_t K, int epilogue,
 proj_status proj_run_candidate(proj_ctx *ctx, int index, const void *X, const void *W,
                                const void *bias, int epilogue, int64_t M, int64_t N,
                                int64_t K, void *Y, int out_dtype, void *stream);
+
+/* The same three for a hi/lo pair (proj_run_hilo's shapes; K is the X row
+ * length). */
+proj_status proj_get_plan_hilo(proj_ctx *ctx, int64_t M, int64_t N, int64_t K, int epilogue,
+                               int out_dtype, int aligned16, char *buf, size_t buflen);
+int proj_num_candidates_hilo(int64_t M, int64_t N, int64_t K, int epilogue, int out_dtype,
+                             int aligned16);
+proj_status proj_candidate_name_hilo(int64_t M, int64_t N, int64_t K, int epilogue,
+                                     int out_dtype, int aligned16, int index, char *buf,
+                                     size_t buflen);
+proj_status proj_run_candidate_hilo(proj_ctx *ctx, int index, const void *X, const void *Whl,
+                                    const void *bias, int epilogue, int64_t M, int64_t N,
+                                    int64_t K, void *Y, int out_dtype, void *stream);
 
 /* HIP-graph capture of repeated launches (hot-path row: capture/replay).
  * Records n_calls proj_run calls, call i using X[i], W[i], bias[i], Y[i]

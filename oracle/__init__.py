@@ -53,6 +53,11 @@ def lib() -> ctypes.CDLL:
         L.oracle_proj_f64_at.argtypes = [u16p, u16p, u16p, ctypes.c_int, i64, i64, i64,
                                          i64p, i64p, i64, dp, ctypes.c_int]
         L.oracle_proj_f64_at.restype = ctypes.c_int
+        f32p = ctypes.POINTER(ctypes.c_float)
+        L.oracle_proj_f64_w32.argtypes = [u16p, f32p, u16p, ctypes.c_int, i64, i64, i64, dp, ctypes.c_int]
+        L.oracle_proj_f64_w32.restype = ctypes.c_int
+        L.oracle_hilo_split.argtypes = [f32p, i64, u16p, u16p]
+        L.oracle_hilo_split.restype = None
         L.oracle_round_out.argtypes = [dp, i64, ctypes.c_int, ctypes.c_void_p]
         L.oracle_round_out.restype = ctypes.c_int
         L.oracle_f64_to_bf16_array.argtypes = [dp, i64, u16p]
@@ -125,6 +130,35 @@ def proj_f64_at(X, W, rows, cols, bias=None, epi=EPI_NONE, nthreads=None) -> np.
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return out
+
+
+def proj_f64_w32(X, W32, bias=None, epi=EPI_NONE, nthreads=None) -> np.ndarray:
+    """As proj_f64 with fp32 weights: X uint16 [M, K] bf16 bits, W32 float32
+    [N, K] values (the router's reference product)."""
+    X, bias = _u16(X), _u16(bias)
+    W32 = np.ascontiguousarray(W32, dtype=np.float32)
+    M, K = X.shape
+    N, K2 = W32.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ: X has K=%d, W has K=%d" % (K, K2))
+    out = np.empty((M, N), dtype=np.float64)
+    rc = lib().oracle_proj_f64_w32(_ptr(X, ctypes.c_uint16), _ptr(W32, ctypes.c_float),
+                                   _ptr(bias, ctypes.c_uint16), int(epi), M, N, K,
+                                   _ptr(out, ctypes.c_double), int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return out
+
+
+def hilo_split(W32):
+    """(hi, lo): uint16 bf16 bit arrays of W32's shape with hi = bf16(w) and
+    lo = bf16(w - hi), both rounded to nearest even."""
+    W32 = np.ascontiguousarray(W32, dtype=np.float32)
+    hi = np.empty(W32.shape, dtype=np.uint16)
+    lo = np.empty(W32.shape, dtype=np.uint16)
+    lib().oracle_hilo_split(_ptr(W32, ctypes.c_float), W32.size, _ptr(hi, ctypes.c_uint16),
+                            _ptr(lo, ctypes.c_uint16))
+    return hi, lo
 
 
 def round_out(s: np.ndarray, out_dtype: int) -> np.ndarray:

@@ -22,7 +22,13 @@
  *   - a bias makes the map affine (section "What makes it linear?"), and the
  *     GEMM + GELU epilogue is applied to the finished product (page
  *     "blackroom" on Devpost, section "How we built it", defect table row on
- *     the FFN intermediate).
+ *     the FFN intermediate);
+ *   - fp32 router weights: the reference product takes the fp32 weights
+ *     themselves (section "The actual error rule, including what L2 means"),
+ *     and the permitted bf16 high/low pair is H = bf16(W), R = W - H,
+ *     L = bf16(R) (section "Why the high-plus-low router scheme helped", and
+ *     the scheme's description under "The actual error rule, including what
+ *     L2 means").
  *
  * Readings where the pages are silent (listed with reasons in the design
  * notes): GELU is the tanh form with constants sqrt(2/pi) and 0.044715; bias
@@ -92,14 +98,23 @@ double oracle_gelu_tanh(double s) {
 }
 
 /* One output cell, before output rounding: the plain weighted sum over
- * k = 0..K-1 in ascending order, then bias, then GELU as requested. */
-static double cell(const uint16_t *X, const uint16_t *W, const uint16_t *bias,
-                   int epi, int64_t K, int64_t m, int64_t n) {
+ * k = 0..K-1 in ascending order, then bias, then GELU as requested.  The
+ * weights are bf16 (W) or, when W32 is given, binary32 (W32); each product of
+ * a bf16 and a binary32 value has at most 8 + 24 significant bits, so it is
+ * exact in double. */
+static double cell(const uint16_t *X, const uint16_t *W, const float *W32,
+                   const uint16_t *bias, int epi, int64_t K, int64_t m, int64_t n) {
     double s = 0.0;
     const uint16_t *xr = X + m * K;
-    const uint16_t *wr = W + n * K;
-    for (int64_t k = 0; k < K; ++k)
-        s += oracle_bf16_to_f64(xr[k]) * oracle_bf16_to_f64(wr[k]);
+    if (W32) {
+        const float *wr = W32 + n * K;
+        for (int64_t k = 0; k < K; ++k)
+            s += oracle_bf16_to_f64(xr[k]) * (double)wr[k];
+    } else {
+        const uint16_t *wr = W + n * K;
+        for (int64_t k = 0; k < K; ++k)
+            s += oracle_bf16_to_f64(xr[k]) * oracle_bf16_to_f64(wr[k]);
+    }
     if (epi == ORACLE_EPI_BIAS || epi == ORACLE_EPI_BIAS_GELU)
         s += oracle_bf16_to_f64(bias[n]);
     if (epi == ORACLE_EPI_GELU || epi == ORACLE_EPI_BIAS_GELU)
@@ -109,6 +124,7 @@ static double cell(const uint16_t *X, const uint16_t *W, const uint16_t *bias,
 
 typedef struct {
     const uint16_t *X, *W, *bias;
+    const float *W32;
     int epi;
     int64_t N, K;
     const int64_t *rows, *cols; /* NULL: dense [M, N] cell order */
@@ -121,7 +137,7 @@ static void *run_job(void *p) {
     for (int64_t i = j->begin; i < j->end; ++i) {
         int64_t m = j->rows ? j->rows[i] : i / j->N;
         int64_t n = j->cols ? j->cols[i] : i % j->N;
-        j->out[i] = cell(j->X, j->W, j->bias, j->epi, j->K, m, n);
+        j->out[i] = cell(j->X, j->W, j->W32, j->bias, j->epi, j->K, m, n);
     }
     return NULL;
 }
@@ -130,8 +146,8 @@ static void *run_job(void *p) {
 
 /* Spread `count` independent cells over threads.  Each cell is still the
  * single ascending-k sum above; threads only decide which cells they do. */
-static int run_cells(const uint16_t *X, const uint16_t *W, const uint16_t *bias,
-                     int epi, int64_t N, int64_t K, const int64_t *rows,
+static int run_cells(const uint16_t *X, const uint16_t *W, const float *W32,
+                     const uint16_t *bias, int epi, int64_t N, int64_t K, const int64_t *rows,
                      const int64_t *cols, int64_t count, double *out,
                      int nthreads) {
     if (nthreads < 1) nthreads = 1;
@@ -142,7 +158,7 @@ static int run_cells(const uint16_t *X, const uint16_t *W, const uint16_t *bias,
     int64_t per = count / nthreads, extra = count % nthreads, at = 0;
     for (int t = 0; t < nthreads; ++t) {
         int64_t len = per + (t < extra ? 1 : 0);
-        job_t j = {X, W, bias, epi, N, K, rows, cols, at, at + len, out};
+        job_t j = {X, W, bias, W32, epi, N, K, rows, cols, at, at + len, out};
         jobs[t] = j;
         at += len;
     }
@@ -157,7 +173,7 @@ static int run_cells(const uint16_t *X, const uint16_t *W, const uint16_t *bias,
     return 0;
 }
 
-static int bad_args(const uint16_t *X, const uint16_t *W, const uint16_t *bias,
+static int bad_args(const uint16_t *X, const void *W, const uint16_t *bias,
                     int epi, int64_t M, int64_t N, int64_t K) {
     if (M < 0 || N < 0 || K < 0) return 1;
     if (epi < ORACLE_EPI_NONE || epi > ORACLE_EPI_BIAS_GELU) return 1;
@@ -173,7 +189,7 @@ int oracle_proj_f64(const uint16_t *X, const uint16_t *W, const uint16_t *bias,
                     int epi, int64_t M, int64_t N, int64_t K, double *out,
                     int nthreads) {
     if (bad_args(X, W, bias, epi, M, N, K) || (!out && M * N > 0)) return -1;
-    return run_cells(X, W, bias, epi, N, K, NULL, NULL, M * N, out, nthreads);
+    return run_cells(X, W, NULL, bias, epi, N, K, NULL, NULL, M * N, out, nthreads);
 }
 
 /* Sampled oracle: out[i] = the same cell value at (rows[i], cols[i]). */
@@ -184,7 +200,31 @@ int oracle_proj_f64_at(const uint16_t *X, const uint16_t *W, const uint16_t *bia
     if (bad_args(X, W, bias, epi, M, N, K) || count < 0) return -1;
     for (int64_t i = 0; i < count; ++i)
         if (rows[i] < 0 || rows[i] >= M || cols[i] < 0 || cols[i] >= N) return -1;
-    return run_cells(X, W, bias, epi, N, K, rows, cols, count, out, nthreads);
+    return run_cells(X, W, NULL, bias, epi, N, K, rows, cols, count, out, nthreads);
+}
+
+/* Dense oracle with fp32 weights W32 [N, K] (the router's reference):
+ * out[m*N + n] = epilogue(sum_k X[m,k] W32[n,k]) in double. */
+int oracle_proj_f64_w32(const uint16_t *X, const float *W32, const uint16_t *bias,
+                        int epi, int64_t M, int64_t N, int64_t K, double *out,
+                        int nthreads) {
+    if (bad_args(X, W32, bias, epi, M, N, K) || (!out && M * N > 0)) return -1;
+    return run_cells(X, NULL, W32, bias, epi, N, K, NULL, NULL, M * N, out, nthreads);
+}
+
+/* The bf16 high/low pair of each fp32 weight: hi = bf16(w) rounded to
+ * nearest even, r = w - hi, lo = bf16(r) rounded to nearest even.  r is
+ * taken in double; it is exact there (and in fp32 too: w and hi share an
+ * exponent range and r needs at most 17 significant bits), so the two
+ * rounding steps are the only approximations. */
+void oracle_hilo_split(const float *w, int64_t count, uint16_t *hi, uint16_t *lo) {
+    for (int64_t i = 0; i < count; ++i) {
+        double x = (double)w[i];
+        uint16_t h = oracle_f64_to_bf16(x);
+        double r = x - oracle_bf16_to_f64(h);
+        hi[i] = h;
+        lo[i] = oracle_f64_to_bf16(r);
+    }
 }
 
 /* Round a double array to the output type: fp32 (float array) or bf16

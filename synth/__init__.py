@@ -115,6 +115,30 @@ def sweep_inputs(s: SweepShape, offset: int = 0):
     return X, W
 
 
+def probe_rows(M: int):
+    """Rows that carry a sparse probe: one row in eight (rows 7, 15, ...),
+    so there is at least one from M = 8 up (worklog, section "The actual
+    error rule, including what L2 means")."""
+    return list(range(7, M, 8))
+
+
+PROBE_NNZ = 8
+
+
+def with_probe_rows(X: np.ndarray, seed: int) -> np.ndarray:
+    """A copy of bf16 bits X whose probe rows are replaced by sparse rows:
+    PROBE_NNZ distinct positions holding N(0, 1) values, zeros elsewhere."""
+    X = np.array(X, dtype=np.uint16, copy=True)
+    M, K = X.shape
+    rng = np.random.Generator(np.random.PCG64(seed))
+    for m in probe_rows(M):
+        X[m, :] = 0
+        nnz = min(PROBE_NNZ, K)
+        cols = rng.choice(K, size=nnz, replace=False)
+        X[m, cols] = f32_to_bf16_bits(rng.standard_normal(nnz, dtype=np.float32))
+    return X
+
+
 def f32_to_bf16_bits(a: np.ndarray, out: np.ndarray | None = None) -> np.ndarray:
     """Round float32 samples to bf16 bit patterns (nearest, ties to even).
     Only used to produce inputs; the samples must be finite."""

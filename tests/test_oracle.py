@@ -328,6 +328,131 @@ def test_epilogue_order_bias_then_gelu():
     assert np.array_equal(oracle.proj_f64(X, W, b, oracle.EPI_GELU), oracle.gelu_tanh(plain))
 
 
+# -------------------------------------------- fp32 weights and the hi/lo pair
+
+def test_hilo_page_example():
+    """The halfway weight of the worklog's hi/lo section: the high part goes
+    to the even neighbour 1.0 and the low part holds the residual exactly."""
+    g = golden()["bf16"]
+    hi, lo = oracle.hilo_split(np.array([g["tie_input"], -g["tie_input"]], np.float32))
+    assert oracle.bf16_to_f64(hi).tolist() == [g["tie_result"], -g["tie_result"]]
+    assert oracle.bf16_to_f64(lo).tolist() == [g["tie_residual"], -g["tie_residual"]]
+    # 1.0 is 0x3F80; 2^-8 has biased exponent 119 and no fraction: 0x3B80
+    assert hi.tolist() == [0x3F80, 0xBF80] and lo.tolist() == [0x3B80, 0xBB80]
+
+
+def _hilo_weights():
+    rng = np.random.default_rng(81)
+    normal = rng.standard_normal(20000).astype(np.float32) * np.float32(1 / 90.5)
+    scaled = (rng.standard_normal(5000) * np.exp2(rng.integers(-120, 120, 5000))).astype(np.float32)
+    # exact bf16 ties and their neighbours: low 16 bits at 0x8000 +- 1
+    top = rng.integers(0, 65536, 3000).astype(np.uint32) << 16
+    ties = (top[:, None] | np.array([0x7FFF, 0x8000, 0x8001], np.uint32)).reshape(-1).view(np.float32)
+    ties = ties[np.isfinite(ties) & (np.abs(ties) < 3e38)]
+    tiny = (rng.standard_normal(2000) * 2.0 ** -130).astype(np.float32)   # bf16 subnormal range
+    special = np.array([0.0, -0.0, 1.0, -2.0, 2.0 ** -126, 2.0 ** -149, 65504.0], np.float32)
+    return np.concatenate([normal, scaled, ties, tiny, special])
+
+
+def test_hilo_vs_bit_trick():
+    """Independent formulation: the integer RNE on float32 bits for both
+    parts, with the residual taken in numpy float32 (where it is exact)."""
+    w = _hilo_weights()
+    hi, lo = oracle.hilo_split(w)
+    ref_hi = _bf16_rne_bit_trick(w)
+    r32 = w - (ref_hi.astype(np.uint32) << 16).view(np.float32)
+    ref_lo = _bf16_rne_bit_trick(r32)
+    assert np.array_equal(hi, ref_hi)
+    assert np.array_equal(lo, ref_lo)
+
+
+def test_hilo_error_bounds():
+    """Two roundings of unit roundoff 2^-8: |lo| <= 2^-8 |w| and
+    |w - (hi + lo)| <= 2^-16 |w| for weights in the normal range; lo is zero
+    exactly when w is itself a bf16 value; signs agree."""
+    w = _hilo_weights()
+    w = w[(np.abs(w) >= 2.0 ** -100) | (w == 0)]
+    hi, lo = oracle.hilo_split(w)
+    wd, hd, ld = w.astype(np.float64), oracle.bf16_to_f64(hi), oracle.bf16_to_f64(lo)
+    assert np.all(np.abs(ld) <= 2.0 ** -8 * np.abs(wd))
+    assert np.all(np.abs(wd - (hd + ld)) <= 2.0 ** -16 * np.abs(wd))
+    is_bf16 = (w.view(np.uint32) & 0xFFFF) == 0
+    assert np.array_equal(ld == 0, is_bf16)
+    assert np.all(np.signbit(hd[wd != 0]) == np.signbit(wd[wd != 0]))
+
+
+def test_hilo_recovers_constructed_pairs():
+    """w = h + l, with h a bf16 value and l a bf16 value small enough that
+    h is w's nearest bf16 value (|l| < 2^-9 of h's binade) and large enough
+    that w is exact in fp32: the split returns (h, l) bit for bit.  A swapped
+    pair or a residual of the wrong sign fails here."""
+    rng = np.random.default_rng(82)
+    n = 4000
+    e = rng.integers(-40, 40, n)
+    h = np.ldexp(1 + rng.integers(0, 128, n) / 128.0, e) * rng.choice([-1.0, 1.0], n)
+    el = e - rng.integers(10, 17, n)
+    l = np.ldexp(1 + rng.integers(0, 128, n) / 128.0, el) * rng.choice([-1.0, 1.0], n)
+    w = (h + l).astype(np.float32)
+    assert np.array_equal(w.astype(np.float64), h + l)      # exact in fp32 by construction
+    hi, lo = oracle.hilo_split(w)
+    assert np.array_equal(oracle.bf16_to_f64(hi), h)
+    assert np.array_equal(oracle.bf16_to_f64(lo), l)
+
+
+def test_w32_matches_numpy_float64_matmul():
+    """fp32 weights: bf16 x fp32 products are exact in double, so numpy's
+    float64 matmul differs only by summation order."""
+    for seed, (M, N, K) in enumerate([(1, 1, 1), (3, 5, 7), (16, 33, 64), (9, 20, 200)]):
+        X = synth.normal_bf16((M, K), 1.0, 300 + seed)
+        W = (np.random.default_rng(400 + seed).standard_normal((N, K)) / math.sqrt(K)).astype(np.float32)
+        Xd, Wd = oracle.bf16_to_f64(X), W.astype(np.float64)
+        ref = Xd @ Wd.T
+        mag = np.abs(Xd) @ np.abs(Wd).T
+        got = oracle.proj_f64_w32(X, W, nthreads=2)
+        assert np.all(np.abs(got - ref) <= 2 * K * 2.0 ** -53 * mag + 1e-300)
+
+
+def test_w32_exact_rationals_and_bias():
+    X = synth.normal_bf16((2, 5), 1.0, 91)
+    W = (np.random.default_rng(92).standard_normal((3, 5))).astype(np.float32)
+    b = synth.normal_bf16((3,), 0.5, 93)
+    Xd, bd = oracle.bf16_to_f64(X), oracle.bf16_to_f64(b)
+    got = oracle.proj_f64_w32(X, W, b, oracle.EPI_BIAS)
+    for m in range(2):
+        for n in range(3):
+            terms = [Fraction(Xd[m, k]) * Fraction(float(W[n, k])) for k in range(5)]
+            exact = sum(terms) + Fraction(bd[n])
+            mag = sum(abs(t) for t in terms) + abs(Fraction(bd[n]))
+            assert abs(Fraction(got[m, n]) - exact) <= Fraction(8 * 2 ** -53) * mag
+    gg = oracle.proj_f64_w32(X, W, b, oracle.EPI_BIAS_GELU)
+    assert np.array_equal(gg, oracle.gelu_tanh(got))
+
+
+def test_w32_agrees_with_bf16_oracle_on_bf16_weights():
+    """Weights that are bf16 values give the same doubles through either
+    weight format (same products, same order)."""
+    X = synth.normal_bf16((6, 130), 1.0, 94)
+    Wb = synth.normal_bf16((7, 130), 0.1, 95)
+    W32 = oracle.bf16_to_f64(Wb).astype(np.float32)
+    assert np.array_equal(oracle.proj_f64_w32(X, W32), oracle.proj_f64(X, Wb))
+
+
+def test_hilo_product_meets_router_tolerance():
+    """The scheme itself: X (hi + lo)^T, computed exactly by the bf16 oracle
+    on the paired layout [hi | lo] with X repeated, differs from the fp32
+    reference by at most 2^-16 sum |x w| per cell, far inside the router's
+    0.01% relative L2."""
+    M, N, K = 8, 64, 512
+    X = synth.normal_bf16((M, K), 1.0, 96)
+    W = (np.random.default_rng(97).standard_normal((N, K)) / math.sqrt(K)).astype(np.float32)
+    hi, lo = oracle.hilo_split(W)
+    pair = oracle.proj_f64(np.concatenate([X, X], axis=1), np.concatenate([hi, lo], axis=1))
+    ref = oracle.proj_f64_w32(X, W)
+    mag = np.abs(oracle.bf16_to_f64(X)) @ np.abs(W.astype(np.float64)).T
+    assert np.all(np.abs(pair - ref) <= 2.0 ** -16 * mag * (1 + 1e-9))
+    assert compare.rel_l2(pair, ref) < 1e-5
+
+
 # ------------------------------------------------------------------ comparator
 
 def test_comparator_rule():
@@ -340,3 +465,38 @@ def test_comparator_rule():
     assert not rep["ok"] and rep["n_bad"] == 1
     assert not compare.check(np.array([np.nan, 1, -10, 100.0]), r)["ok"]
     assert not compare.check(np.array([np.inf, 1, -10, 100.0]), r)["ok"]
+
+
+def test_row_rule():
+    """The worklog's row rule: whole-output relative L2 within the
+    tolerance, each row within five times it against max(own norm, a tenth
+    of the mean row norm), sparse probe rows within 0.1%."""
+    g = golden()["rel_l2"]
+    r = np.array([g["r"]], dtype=np.float64)
+    u = np.array([g["u"]], dtype=np.float64)
+    assert abs(compare.check_rows(u, r, tol=1.0)["rel_l2"] - g["value"]) < 1e-12
+    assert compare.check_rows(u, r, tol=0.0101)["ok"]
+    assert not compare.check_rows(u, r, tol=0.0099)["ok"]
+    rng = np.random.default_rng(3)
+    r = rng.standard_normal((100, 64))
+    u = r * (1 + 1e-6)
+    assert compare.check_rows(u, r)["ok"]
+    # one bad row hidden in a good average: 6e-4 relative on a single row
+    bad = u.copy()
+    bad[5] = r[5] * (1 + 6e-4)
+    rep = compare.check_rows(bad, r)
+    assert rep["rel_l2"] <= compare.ROUTER_TOL and not rep["ok"]
+    # a near-zero row is judged against a tenth of the mean row norm
+    r2 = r.copy()
+    r2[9] = 1e-9
+    u2 = r2.copy()
+    u2[9] += 1e-5
+    assert compare.check_rows(u2, r2)["ok"]
+    # probe rows: 0.1% of their own norm
+    u3 = r.copy()
+    u3[7] = r[7] * (1 + 2e-4)
+    assert compare.check_rows(u3, r, tol=1e-3, probe_rows=[7])["ok"]
+    u3[7] = r[7] * (1 + 2e-3)
+    assert not compare.check_rows(u3, r, tol=1e-2, probe_rows=[7])["ok"]
+    assert not compare.check_rows(np.full((2, 2), np.nan), np.ones((2, 2)))["ok"]
+    assert not compare.check_rows(np.ones((2, 3)), np.ones((2, 2)))["ok"]

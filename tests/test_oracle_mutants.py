@@ -15,8 +15,10 @@ import tests.test_oracle as pins
 SRC = open(oracle.SRC).read()
 
 MUTANTS = {
-    "drops_last_term": ("for (int64_t k = 0; k < K; ++k)\n        s +=",
-                        "for (int64_t k = 0; k + 1 < K; ++k)\n        s +="),
+    "drops_last_term": ("for (int64_t k = 0; k < K; ++k)\n            s += oracle_bf16_to_f64(xr[k]) * oracle_bf16_to_f64",
+                        "for (int64_t k = 0; k + 1 < K; ++k)\n            s += oracle_bf16_to_f64(xr[k]) * oracle_bf16_to_f64"),
+    "w32_drops_last_term": ("for (int64_t k = 0; k < K; ++k)\n            s += oracle_bf16_to_f64(xr[k]) * (double)",
+                            "for (int64_t k = 0; k + 1 < K; ++k)\n            s += oracle_bf16_to_f64(xr[k]) * (double)"),
     "transposed_operand": ("const uint16_t *wr = W + n * K;", "const uint16_t *wr = W + m * K;"),
     "bias_sign": ("s += oracle_bf16_to_f64(bias[n]);", "s -= oracle_bf16_to_f64(bias[n]);"),
     "bias_wrong_index": ("s += oracle_bf16_to_f64(bias[n]);", "s += oracle_bf16_to_f64(bias[0]);"),
@@ -29,6 +31,14 @@ MUTANTS = {
                            "if (v >= 0x1p128) return (uint16_t)(sign | 0x7F7Fu);"),
     "decode_shift": ("(uint32_t)bits << 16", "(uint32_t)bits << 15"),
     "fraction_bits": ("int q = (e - 1) - 7;", "int q = (e - 1) - 8;"),
+    "hilo_residual_sign": ("double r = x - oracle_bf16_to_f64(h);", "double r = oracle_bf16_to_f64(h) - x;"),
+    "hilo_hi_truncates": ("uint16_t h = oracle_f64_to_bf16(x);",
+                          "float xf_ = (float)x; uint32_t u_; memcpy(&u_, &xf_, 4); uint16_t h = (uint16_t)(u_ >> 16);"),
+    "hilo_lo_truncates": ("lo[i] = oracle_f64_to_bf16(r);",
+                          "float rf_ = (float)r; uint32_t v_; memcpy(&v_, &rf_, 4); lo[i] = (uint16_t)(v_ >> 16);"),
+    "w32_weights_rounded_to_bf16": ("s += oracle_bf16_to_f64(xr[k]) * (double)wr[k];",
+                                    "s += oracle_bf16_to_f64(xr[k]) * oracle_bf16_to_f64(oracle_f64_to_bf16(wr[k]));"),
+    "w32_transposed_operand": ("const float *wr = W32 + n * K;", "const float *wr = W32 + m * K;"),
 }
 
 PIN_TESTS = [
@@ -46,6 +56,13 @@ PIN_TESTS = [
     pins.test_gelu_tanh_vs_torch_float64,
     pins.test_gelu_identities_and_limits,
     pins.test_epilogue_order_bias_then_gelu,
+    pins.test_hilo_page_example,
+    pins.test_hilo_vs_bit_trick,
+    pins.test_hilo_error_bounds,
+    pins.test_hilo_recovers_constructed_pairs,
+    pins.test_w32_matches_numpy_float64_matmul,
+    pins.test_w32_exact_rationals_and_bias,
+    pins.test_w32_agrees_with_bf16_oracle_on_bf16_weights,
 ]
 
 
@@ -67,7 +84,8 @@ def test_pins_catch_mutant(tmp_path, name, monkeypatch):
     # load the mutant with the real library's signatures
     mut = ctypes.CDLL(so)
     for fn in ("oracle_proj_f64", "oracle_proj_f64_at", "oracle_round_out", "oracle_f64_to_bf16_array",
-               "oracle_bf16_to_f64_array", "oracle_gelu_tanh_array"):
+               "oracle_bf16_to_f64_array", "oracle_gelu_tanh_array", "oracle_proj_f64_w32",
+               "oracle_hilo_split"):
         f, g = getattr(mut, fn), getattr(real, fn)
         f.argtypes, f.restype = g.argtypes, g.restype
     monkeypatch.setattr(oracle, "_lib", mut)
