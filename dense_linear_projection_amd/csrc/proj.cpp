@@ -122,6 +122,9 @@ class DeviceGuard {
     int prev_ = -1;
 };
 
+// largest M offered to the streaming kernel (in 64- or 128-row blocks)
+constexpr int64_t kStreamMaxM = 512;
+
 int mt_for(int64_t M) {
     const int64_t need = (M + 15) / 16;
     return need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 0;
@@ -148,24 +151,31 @@ std::string gemm_name(const GemmVariant &v, int S) {
 std::vector<Candidate> candidates(const Key &k) {
     std::vector<Candidate> out;
     if (k.aligned && k.K > 0) {
+        // row blocks of the streaming kernel: the one block size that covers
+        // M up to 64 rows; above that, 64- or 128-row blocks up to
+        // kStreamMaxM rows (one block of W rows is then read once per row
+        // block)
         const int mt = mt_for(k.M);
-        if (mt > 0) {
+        auto mt_ok = [&](int vmt) { return mt > 0 ? vmt == mt : k.M <= kStreamMaxM && (vmt == 4 || vmt == 8); };
+        if (mt > 0 || k.M <= kStreamMaxM) {
             for (int i = 0; i < kNumStreamVariants; ++i) {
                 const StreamVariant &v = kStreamVariants[i];
-                if (v.mt != mt) continue;
+                if (!mt_ok(v.mt)) continue;
+                const int64_t mblocks = (k.M + 16 * v.mt - 1) / (16 * v.mt);
+                const int64_t rows_x = k.M < 16 * v.mt ? k.M : 16 * v.mt;
                 // a hi/lo pair is read on the buffer-resource path only: whole
                 // stages, the X wrap at K/2 on a stage boundary, and operand
                 // offsets that fit its 32-bit resources
                 if (k.hilo && (k.K % v.kc != 0 || (k.K / 2) % v.kc != 0 ||
-                               k.M * (k.K / 2) * 2 >= (int64_t{1} << 32) ||
+                               rows_x * (k.K / 2) * 2 >= (int64_t{1} << 32) ||
                                int64_t{16} * v.nt * k.K * 2 >= (int64_t{1} << 32)))
                     continue;
                 const int64_t stages = (k.K + v.kc - 1) / v.kc;
                 const int64_t tiles = (k.N + 16 * v.nt - 1) / (16 * v.nt);
-                for (int S : {1, 2, 4, 8}) {
+                for (int S : {1, 2, 4, 8, 16}) {
                     if (S > 1 && S > stages) continue;
                     if (S > 1 && static_cast<size_t>(S) * k.M * k.N * sizeof(float) > kWorkspaceBytes) continue;
-                    if (tiles * S > 0x7fffffff) continue;
+                    if (mblocks * tiles * S > 0x7fffffff) continue;
                     out.push_back({KIND_STREAM, i, S, stream_name(v, S)});
                 }
             }

@@ -1,5 +1,5 @@
-// stream.hip -- weight-streaming projection for few token rows (M <= 64),
-// staged through an LDS ring filled by global->LDS DMA.
+// stream.hip -- weight-streaming projection for few token rows, staged
+// through an LDS ring filled by global->LDS DMA.
 //
 // At small M each weight is used by only M token rows, so the projection is
 // bound by reading W once (worklog "How I made Muse's GPU projections 1.32x
@@ -9,7 +9,9 @@
 // doing the little arithmetic on the side.
 //
 // Decomposition:
-//   * a workgroup owns 16*NT output features (W rows) and one of S
+//   * a workgroup owns 16*MT token rows (one of ceil(M / 16*MT) row blocks;
+//     the row block is the slowest-varying part of the workgroup index),
+//     16*NT output features (W rows) and one of S
 //     contiguous ranges of K, cut at KC-element stage boundaries as evenly
 //     as integers allow (stages floor(s*T/S) .. floor((s+1)*T/S)); with S > 1
 //     each range writes an fp32 partial tile and a second kernel adds the S
@@ -95,9 +97,15 @@ __global__ __launch_bounds__(WAVES * 64) void stream_kernel(Args a, int S) {
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int tile = blockIdx.x / S, split = blockIdx.x % S;
-    const int64_t K = a.K, M = a.M, N = a.N;
+    const int64_t K = a.K, N = a.N;
+    const int64_t tiles = (N + C::NR - 1) / C::NR;
+    const int64_t mb = blockIdx.x / (tiles * S);
+    const int tile = static_cast<int>((blockIdx.x % (tiles * S)) / S), split = blockIdx.x % S;
     const int64_t n0 = static_cast<int64_t>(tile) * C::NR;
+    // this workgroup's token rows: m0 .. m0 + M - 1 (M counted from m0)
+    const int64_t m0 = mb * C::MR;
+    const int64_t M = (a.M - m0) < C::MR ? (a.M - m0) : C::MR;
+    const uint16_t *X = a.X + m0 * a.kx;
 
     // stage range of this split, and the rotated walk over it
     const int64_t T = (K + KC - 1) / KC;
@@ -125,7 +133,7 @@ __global__ __launch_bounds__(WAVES * 64) void stream_kernel(Args a, int S) {
             src[j] = n < N ? a.W + n * K + chunk * 8 : nullptr;
         } else {
             const int64_t m = row - C::NR;
-            src[j] = m < M ? a.X + m * K + chunk * 8 : nullptr;
+            src[j] = m < M ? X + m * K + chunk * 8 : nullptr;
         }
     }
     // FAST: resources over the tile's valid W rows and over X, and each
@@ -153,7 +161,7 @@ __global__ __launch_bounds__(WAVES * 64) void stream_kernel(Args a, int S) {
             // X column of a hi/lo pair's second half wraps to the start
             const uint32_t soffx = static_cast<uint32_t>((k0 >= a.kx ? k0 - a.kx : k0) * 2);
             const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(a.W + n0 * K, live ? wbytes : 0u);
-            const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(a.X, live ? xbytes : 0u);
+            const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(X, live ? xbytes : 0u);
 #pragma unroll
             for (int j = 0; j < C::PERW; ++j) {
                 const bool is_w = (wave + j * WAVES) * C::RPI < C::NR;  // wave-uniform
@@ -251,9 +259,9 @@ __global__ __launch_bounds__(WAVES * 64) void stream_kernel(Args a, int S) {
         if (m >= M || n >= N) continue;
         if (S == 1) {
             const float b = (a.epi & 1) ? bf16_bits_to_f32(bias[n]) : 0.f;
-            store_out(a.Y, a.out, m * N + n, apply_epilogue(s, a.epi, b));
+            store_out(a.Y, a.out, (m0 + m) * N + n, apply_epilogue(s, a.epi, b));
         } else {
-            a.ws[(static_cast<int64_t>(split) * M + m) * N + n] = s;
+            a.ws[(static_cast<int64_t>(split) * a.M + m0 + m) * N + n] = s;
         }
     }
 }
@@ -282,7 +290,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(Args a, int S) {
     X(1, 2, 4, 128, 5, 1) X(1, 1, 8, 256, 4, 1) X(2, 4, 4, 128, 4, 1)                                      \
     X(4, 7, 4, 128, 3, 1) X(4, 4, 4, 128, 4, 1) X(4, 2, 4, 128, 6, 1)                                      \
     X(1, 2, 4, 128, 4, 1) X(1, 2, 4, 128, 6, 1) X(1, 2, 4, 128, 7, 1) X(1, 1, 4, 128, 6, 1)                \
-    X(1, 4, 4, 128, 4, 1) X(1, 2, 8, 256, 4, 1) X(1, 2, 8, 256, 3, 1) X(1, 1, 4, 128, 9, 1)
+    X(1, 4, 4, 128, 4, 1) X(1, 2, 8, 256, 4, 1) X(1, 2, 8, 256, 3, 1) X(1, 1, 4, 128, 9, 1)                \
+    X(8, 1, 4, 128, 4, 0) X(8, 2, 4, 128, 3, 0) X(8, 4, 4, 128, 3, 0)                                      \
+    X(8, 1, 4, 128, 4, 1) X(8, 2, 4, 128, 3, 1) X(8, 4, 4, 128, 3, 1)
 
 #define PROJ_STREAM_INST(MT, NT, WV, KC, D, WNT)                                  \
     template __global__ void stream_kernel<MT, NT, WV, KC, D, WNT, false>(Args, int); \
@@ -304,13 +314,15 @@ static hipError_t prepare_stream() {
 template <int MT, int NT, int WV, int KC, int D, int WNT>
 static hipError_t launch_stream(const Args &a, int S, hipStream_t st) {
     const int64_t tiles = (a.N + 16 * NT - 1) / (16 * NT);
-    const int64_t grid = tiles * S;
+    const int64_t mblocks = (a.M + 16 * MT - 1) / (16 * MT);
+    const int64_t grid = mblocks * tiles * S;
     if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     constexpr int lds_bytes = StreamCfg<MT, NT, WV, KC, D>::LDS;
     // the buffer-resource path needs whole stages and 32-bit operand offsets;
     // it is also the only one that reads a hi/lo pair's X (kx < K), whose
     // wrap must fall on a stage boundary
-    const bool fast = a.K % KC == 0 && a.kx % KC == 0 && a.M * a.kx * 2 < (int64_t{1} << 32) &&
+    const int64_t rows_x = a.M < 16 * MT ? a.M : 16 * MT;  // X rows one workgroup addresses
+    const bool fast = a.K % KC == 0 && a.kx % KC == 0 && rows_x * a.kx * 2 < (int64_t{1} << 32) &&
                       16 * NT * a.K * 2 < (int64_t{1} << 32);
     if (!fast && a.kx != a.K) return hipErrorInvalidValue;
     if (fast)

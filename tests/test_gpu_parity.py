@@ -44,6 +44,8 @@ INT_SHAPES = [
     (300, 520, 512),   # large-M family, ragged M and N
     (257, 129, 128),
     (300, 256, 64),    # large-M family, a single 64-wide k-range
+    (130, 200, 1024),  # streaming kernel in row blocks: the last holds 2 rows
+    (385, 96, 512),    # 4 row blocks of 128 (7 of 64), the last holds 1 row
 ]
 
 
