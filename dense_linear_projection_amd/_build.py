@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libproj.so")
-SOURCES = ["proj.cpp", "stream.hip", "gemm.hip", "generic.hip"]
+SOURCES = ["proj.cpp", "stream.hip", "gemm.hip", "gemv.hip", "generic.hip"]
 
 
 def hipcc() -> str:

@@ -30,6 +30,16 @@ struct GemmVariant {
 extern const GemmVariant kGemmVariants[];
 extern const int kNumGemmVariants;
 
+// Few token rows (M <= mr), W rows streamed into registers (gemv.hip).
+struct GemvVariant {
+    const char *family;
+    int mr, rows, waves, unroll;  // token rows, W rows per workgroup, waves, chunks per row per iteration
+    int wnt;                      // W loads carry the non-temporal hint
+    hipError_t (*launch)(const Args &, int splits, hipStream_t);
+};
+extern const GemvVariant kGemvVariants[];
+extern const int kNumGemvVariants;
+
 // Second pass of split-K (stream.hip): Y = epilogue(sum over the S fp32
 // partials in a.ws, in split order).
 hipError_t launch_splitk_reduce(const Args &a, int S, hipStream_t st);

@@ -49,7 +49,7 @@ struct Key {
     }
 };
 
-enum Kind { KIND_STREAM = 0, KIND_GEMM = 1, KIND_GENERIC = 2 };
+enum Kind { KIND_STREAM = 0, KIND_GEMM = 1, KIND_GENERIC = 2, KIND_GEMV = 3 };
 
 struct Candidate {
     Kind kind;
@@ -137,6 +137,12 @@ std::string stream_name(const StreamVariant &v, int S) {
     return b;
 }
 
+std::string gemv_name(const GemvVariant &v, int S) {
+    char b[96];
+    snprintf(b, sizeof b, "gemv_m%d_r%d_w%d_u%d%s_s%d", v.mr, v.rows, v.waves, v.unroll, v.wnt ? "_wnt" : "", S);
+    return b;
+}
+
 std::string gemm_name(const GemmVariant &v, int S) {
     char b[96];
     snprintf(b, sizeof b, "%s_%dx%dx%d_w%dx%d_g%d", v.family, v.bm, v.bn, v.bk, v.waves_m, v.waves_n, v.group_m);
@@ -177,6 +183,23 @@ std::vector<Candidate> candidates(const Key &k) {
                     if (S > 1 && static_cast<size_t>(S) * k.M * k.N * sizeof(float) > kWorkspaceBytes) continue;
                     if (mblocks * tiles * S > 0x7fffffff) continue;
                     out.push_back({KIND_STREAM, i, S, stream_name(v, S)});
+                }
+            }
+        }
+        // register-streaming GEMV: the smallest token-row count that covers
+        // M (up to 8), whole 16-byte chunks, offsets in the 31-bit range
+        const int mr = k.M <= 1 ? 1 : k.M <= 2 ? 2 : k.M <= 4 ? 4 : k.M <= 8 ? 8 : 0;
+        const int64_t kxk = k.hilo ? k.K / 2 : k.K;
+        if (mr > 0 && kxk % 8 == 0 && k.M * kxk * 2 <= 0x7fffffff) {
+            for (int i = 0; i < kNumGemvVariants; ++i) {
+                const GemvVariant &v = kGemvVariants[i];
+                if (v.mr != mr || static_cast<int64_t>(v.rows) * k.K * 2 > 0x7fffffff) continue;
+                const int64_t tiles = (k.N + v.rows - 1) / v.rows;
+                for (int S : {1, 2, 4, 8}) {
+                    if (S > 1 && S > k.K / 8) continue;
+                    if (S > 1 && static_cast<size_t>(S) * k.M * k.N * sizeof(float) > kWorkspaceBytes) continue;
+                    if (tiles * S > 0x7fffffff) continue;
+                    out.push_back({KIND_GEMV, i, S, gemv_name(v, S)});
                 }
             }
         }
@@ -253,6 +276,7 @@ hipError_t launch(const Candidate &cand, const Args &a, hipStream_t st) {
     switch (cand.kind) {
         case KIND_GEMM: return kGemmVariants[cand.variant].launch(a, cand.splits, st);
         case KIND_STREAM: return kStreamVariants[cand.variant].launch(a, cand.splits, st);
+        case KIND_GEMV: return kGemvVariants[cand.variant].launch(a, cand.splits, st);
         default: return launch_generic(a, st);
     }
 }

@@ -98,9 +98,10 @@ __global__ __launch_bounds__(WAVES * 64) void stream_kernel(Args a, int S) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t K = a.K, N = a.N;
-    const int64_t tiles = (N + C::NR - 1) / C::NR;
-    const int64_t mb = blockIdx.x / (tiles * S);
-    const int tile = static_cast<int>((blockIdx.x % (tiles * S)) / S), split = blockIdx.x % S;
+    // the launcher keeps the grid (row blocks x tiles x S) below 2^31
+    const uint32_t tS = static_cast<uint32_t>((N + C::NR - 1) / C::NR) * static_cast<uint32_t>(S);
+    const int64_t mb = blockIdx.x / tS;
+    const int tile = static_cast<int>((blockIdx.x % tS) / static_cast<uint32_t>(S)), split = blockIdx.x % S;
     const int64_t n0 = static_cast<int64_t>(tile) * C::NR;
     // this workgroup's token rows: m0 .. m0 + M - 1 (M counted from m0)
     const int64_t m0 = mb * C::MR;

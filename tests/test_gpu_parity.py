@@ -68,7 +68,9 @@ def test_every_candidate_bit_exact_on_integers(ctx, shape):
                     name, epi, out, bad[0], u[tuple(bad[0])], r[tuple(bad[0])])
 
 
-RAND_SHAPES = [(16, 1040, 2048), (64, 200, 1024), (17, 64, 512), (520, 384, 640)]
+RAND_SHAPES = [(16, 1040, 2048), (64, 200, 1024), (17, 64, 512), (520, 384, 640),
+               (3, 1000, 2056),   # register-streaming GEMV: ragged chunk count (257 per row), N % 16 == 8
+               (8, 300, 4096)]    # GEMV at its largest token count
 
 
 @pytest.mark.parametrize("shape", RAND_SHAPES, ids=lambda s: "M%d_N%d_K%d" % s)
