@@ -91,7 +91,8 @@ def stream_plan_launch(plan: str, w):
     fast = w.K % kc == 0  # whole stages take the buffer-resource copy path
     name = "stream_kernel<%d, %d, %d, %d, %d, %d, %s>" % (mt, nt, waves, kc, d, int(wnt), "true" if fast else "false")
     tiles = -(-w.N // (16 * nt))
-    return name, tiles * S * waves * 64
+    mblocks = -(-w.M // (16 * mt))
+    return name, mblocks * tiles * S * waves * 64
 
 
 def _pmc_per_dispatch(run_dir: str, counter: str, name_part: str, skip_first: int = 0, grid: int = 0):
