@@ -389,6 +389,51 @@ def sweep(args) -> int:
     return 0
 
 
+def time_packed(ctx, w, args, Xs, Ws, bs, Ys, idx, stream) -> dict:
+    """The same steps with W registered once in the packed tile layout
+    (proj_pack_weights, outside the timed region), run by proj_run_packed;
+    the R calls are captured in a torch CUDA graph (the library's own graph
+    helper takes row-major weights)."""
+    import torch
+
+    import dense_linear_projection_amd as dlp
+
+    t16, P, R = args.packed, len(Xs), len(idx)
+    Wps = [dlp.proj_pack_weights(ctx, Ws[p], t16, stream=stream) for p in range(P)]
+    with torch.cuda.stream(stream):
+        for p in range(P):                       # plan tuning happens on the first call
+            dlp.proj_run_packed(ctx, Xs[p], Wps[p], t16, bs[p], w.epi, Ys[p], w.N, stream=stream)
+    stream.synchronize()
+    plan = dlp.proj_get_plan_packed(ctx, w.M, w.N, w.K, t16, w.epi, w.out_dtype)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in idx:
+            dlp.proj_run_packed(ctx, Xs[i], Wps[i], t16, bs[i], w.epi, Ys[i], w.N, stream=stream)
+    reps = max(1, args.steps // R)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, args.warmup // R)):
+            g.replay()
+        stream.synchronize()
+        trial_us = []
+        for _ in range(5):
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+            e1.synchronize()
+            trial_us.append(e0.elapsed_time(e1) * 1e3 / (reps * R))
+    del g
+    trial_us.sort()
+    us = trial_us[0 + len(trial_us) // 2]
+    sec = us * 1e-6
+    return {"tile16": t16, "plan": plan, "median_us": round(us, 3), "min_us": round(trial_us[0], 3),
+            "max_us": round(trial_us[-1], 3), "gbs": round(w.alg_bytes() / sec / 1e9, 1),
+            "tflops": round(w.alg_flops() / sec / 1e12, 2),
+            "note": "W packed once before timing (registration); five trials of the same steps, median"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -405,6 +450,10 @@ def main() -> int:
     ap.add_argument("--sweep", action="store_true",
                     help="time the thirty-shape set (per load; torch alongside as context) instead of one workload")
     ap.add_argument("--sweep-steps", type=int, default=400, help="calls timed per shape in --sweep")
+    ap.add_argument("--packed", type=int, default=-1, metavar="TILE16",
+                    help="also time the path with W registered in the packed tile layout of 16*TILE16 rows "
+                         "(packing outside the timed region; reported beside the row-major figure). "
+                         "-1: the tile height of the row-major plan, for weight-streaming workloads; 0: off")
     ap.add_argument("--plans", nargs="+", default=[],
                     help="for --ingest: one-pass stream plans to take counters for")
     args = ap.parse_args()
@@ -538,6 +587,12 @@ def main() -> int:
             "note": "one buffer set (P=1): operands resident in the 256 MiB last-level cache, not an HBM rate"}
     dlp.proj_graph_destroy(g_warm)
 
+    packed = None
+    if args.packed < 0 and plan.startswith("stream_"):
+        args.packed = int(plan.split("_nt")[1].split("_")[0])
+    if args.packed > 0:
+        packed = time_packed(ctx, w, args, Xs, Ws, bs, Ys, idx, stream)
+
     dlp.proj_graph_destroy(g)
     if g_tail is not None:
         dlp.proj_graph_destroy(g_tail)
@@ -565,6 +620,8 @@ def main() -> int:
         "trials": trials,
         "warm": warm,
     }
+    if packed is not None:
+        line["packed_weights"] = packed
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, X, W, b, args.cpu_seconds)
     else:

@@ -13,7 +13,11 @@ Names mirror the C ABI: ``proj_create``, ``proj_run``, ``proj_destroy``,
 ``proj_graph_launch``, ``proj_graph_destroy``, ``proj_status_string``, and
 for fp32 weights held as a bf16 high/low pair ``proj_prepare_hilo``,
 ``proj_run_hilo``, ``proj_get_plan_hilo``, ``proj_num_candidates_hilo``,
-``proj_candidate_name_hilo``, ``proj_run_candidate_hilo``.
+``proj_candidate_name_hilo``, ``proj_run_candidate_hilo``, and for bf16
+weights registered in the packed tile layout ``proj_packed_bytes``,
+``proj_pack_weights``, ``proj_run_packed``, ``proj_get_plan_packed``,
+``proj_num_candidates_packed``, ``proj_candidate_name_packed``,
+``proj_run_candidate_packed``.
 """
 from __future__ import annotations
 
@@ -38,7 +42,9 @@ EXPORTS = ["proj_create", "proj_run", "proj_tune", "proj_destroy", "proj_status_
            "proj_last_error", "proj_get_plan", "proj_num_candidates", "proj_candidate_name",
            "proj_run_candidate", "proj_graph_capture", "proj_graph_launch", "proj_graph_destroy",
            "proj_prepare_hilo", "proj_run_hilo", "proj_get_plan_hilo", "proj_num_candidates_hilo",
-           "proj_candidate_name_hilo", "proj_run_candidate_hilo"]
+           "proj_candidate_name_hilo", "proj_run_candidate_hilo", "proj_packed_bytes", "proj_pack_weights",
+           "proj_run_packed", "proj_get_plan_packed", "proj_num_candidates_packed", "proj_candidate_name_packed",
+           "proj_run_candidate_packed"]
 
 
 class ProjError(RuntimeError):
@@ -83,6 +89,13 @@ def lib() -> ctypes.CDLL:
         "proj_num_candidates_hilo": ([i64, i64, i64, ci, ci, ci], ci),
         "proj_candidate_name_hilo": ([i64, i64, i64, ci, ci, ci, ci, ctypes.c_char_p, ctypes.c_size_t], st),
         "proj_run_candidate_hilo": ([vp, ci, vp, vp, vp, ci, i64, i64, i64, vp, ci, vp], st),
+        "proj_packed_bytes": ([i64, i64, ci], i64),
+        "proj_pack_weights": ([vp, vp, i64, i64, ci, vp, vp], st),
+        "proj_run_packed": ([vp, vp, vp, ci, vp, ci, i64, i64, i64, vp, ci, vp], st),
+        "proj_get_plan_packed": ([vp, i64, i64, i64, ci, ci, ci, ci, ctypes.c_char_p, ctypes.c_size_t], st),
+        "proj_num_candidates_packed": ([i64, i64, i64, ci, ci, ci, ci], ci),
+        "proj_candidate_name_packed": ([i64, i64, i64, ci, ci, ci, ci, ci, ctypes.c_char_p, ctypes.c_size_t], st),
+        "proj_run_candidate_packed": ([vp, ci, vp, vp, ci, vp, ci, i64, i64, i64, vp, ci, vp], st),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -284,6 +297,69 @@ def proj_run_candidate_hilo(ctx, index, X, Whl, bias, epilogue, Y, M=None, N=Non
     M, N, K = _shape_hilo(X, Whl, M, N, K)
     _check(lib().proj_run_candidate_hilo(ctx, int(index), _ptr(X), _ptr(Whl), _ptr(bias), int(epilogue), M, N, K,
                                          _ptr(Y), _out_dtype(Y, out_dtype), _stream(stream)), ctx)
+
+
+def proj_packed_bytes(N, K, tile16) -> int:
+    """Bytes of the packed array for W [N, K] in tiles of 16 * tile16 rows
+    (-1 if that packing is not offered)."""
+    return int(lib().proj_packed_bytes(int(N), int(K), int(tile16)))
+
+
+def proj_pack_weights(ctx, W, tile16, Wp=None, stream=None):
+    """Pack bf16 W [N, K] into the tile layout (Wp allocated here if not
+    given: a flat bf16 tensor of proj_packed_bytes / 2 elements); returns Wp."""
+    import torch
+    if W.dtype != torch.bfloat16 or W.dim() != 2:
+        raise ValueError("W must be a bfloat16 [N, K] tensor")
+    N, K = W.shape
+    nbytes = proj_packed_bytes(N, K, tile16)
+    if nbytes < 0:
+        raise ValueError("no packing for N=%d K=%d tile16=%d" % (N, K, tile16))
+    if Wp is None:
+        Wp = torch.empty((nbytes // 2,), dtype=torch.bfloat16, device=W.device)
+    elif Wp.dtype != torch.bfloat16 or Wp.numel() * 2 < nbytes:
+        raise ValueError("Wp must be bfloat16 with at least %d bytes" % nbytes)
+    _check(lib().proj_pack_weights(ctx, _ptr(W), int(N), int(K), int(tile16), _ptr(Wp), _stream(stream)), ctx)
+    return Wp
+
+
+def proj_run_packed(ctx, X, Wp, tile16, bias, epilogue, Y, N, M=None, K=None, out_dtype=None, stream=None) -> None:
+    """Enqueue Y = epilogue(X . W^T [+ bias]) with W given packed (Wp from
+    proj_pack_weights with the same tile16); N is W's row count."""
+    _check_operands(X, Wp, bias, Y)
+    M = int(X.shape[0] if M is None else M)
+    K = int(X.shape[1] if K is None else K)
+    _check(lib().proj_run_packed(ctx, _ptr(X), _ptr(Wp), int(tile16), _ptr(bias), int(epilogue), M, int(N), K,
+                                 _ptr(Y), _out_dtype(Y, out_dtype), _stream(stream)), ctx)
+
+
+def proj_get_plan_packed(ctx, M, N, K, tile16, epilogue, out_dtype, aligned16=True) -> str:
+    buf = ctypes.create_string_buffer(256)
+    _check(lib().proj_get_plan_packed(ctx, int(M), int(N), int(K), int(tile16), int(epilogue), int(out_dtype),
+                                      1 if aligned16 else 0, buf, 256), ctx)
+    return buf.value.decode()
+
+
+def proj_num_candidates_packed(M, N, K, tile16, epilogue, out_dtype, aligned16=True) -> int:
+    return int(lib().proj_num_candidates_packed(int(M), int(N), int(K), int(tile16), int(epilogue), int(out_dtype),
+                                                1 if aligned16 else 0))
+
+
+def proj_candidate_name_packed(M, N, K, tile16, epilogue, out_dtype, index, aligned16=True) -> str:
+    buf = ctypes.create_string_buffer(256)
+    _check(lib().proj_candidate_name_packed(int(M), int(N), int(K), int(tile16), int(epilogue), int(out_dtype),
+                                            1 if aligned16 else 0, int(index), buf, 256))
+    return buf.value.decode()
+
+
+def proj_run_candidate_packed(ctx, index, X, Wp, tile16, bias, epilogue, Y, N, M=None, K=None, out_dtype=None,
+                              stream=None) -> None:
+    _check_operands(X, Wp, bias, Y)
+    M = int(X.shape[0] if M is None else M)
+    K = int(X.shape[1] if K is None else K)
+    _check(lib().proj_run_candidate_packed(ctx, int(index), _ptr(X), _ptr(Wp), int(tile16), _ptr(bias),
+                                           int(epilogue), M, int(N), K, _ptr(Y), _out_dtype(Y, out_dtype),
+                                           _stream(stream)), ctx)
 
 
 def proj_graph_capture(ctx, Xs, Ws, biases, Ys, epilogue, out_dtype=None, stream=None) -> int:

@@ -24,6 +24,7 @@ struct Args {
     int64_t M, N, K;
     int64_t kx;            // X row length: K, or K/2 for a hi/lo weight pair (X column k' reads k' mod kx)
     int epi, out;
+    int wpack = 0;         // 0: W row-major [N][K]; t > 0: W packed in tiles of 16t rows (see proj_pack_weights)
     float *ws;             // split-K partials [S][M][N] (library-owned)
     const uint16_t *zeros; // >= 64 zero bytes in device memory, for masked loads
 };

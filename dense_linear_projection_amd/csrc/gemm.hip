@@ -991,7 +991,7 @@ static hipError_t prepare_gemm() {
 // context is created), so launching is capture-safe.
 template <int BM, int BN, int BK, int WM, int WN, int GM>
 static hipError_t launch_gemm(const Args &a, int S, hipStream_t st) {
-    if (S != 1 || a.kx != a.K) return hipErrorInvalidValue;  // no K split, no hi/lo pair
+    if (S != 1 || a.kx != a.K || a.wpack) return hipErrorInvalidValue;  // no K split, hi/lo pair or packed W
     const int64_t G = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
     if (G <= 0 || G > 0x7fffffff) return hipErrorInvalidConfiguration;
     constexpr int lds_bytes = 2 * (BM + BN) * BK * 2;
@@ -1013,7 +1013,7 @@ static hipError_t prepare_gemm_pp() {
 
 template <int BN, int GM>
 static hipError_t launch_gemm_pp(const Args &a, int S, hipStream_t st) {
-    if (S != 1 || a.kx != a.K) return hipErrorInvalidValue;  // no K split, no hi/lo pair
+    if (S != 1 || a.kx != a.K || a.wpack) return hipErrorInvalidValue;  // no K split, hi/lo pair or packed W
     const int64_t G = ((a.M + 255) / 256) * ((a.N + BN - 1) / BN);
     if (G <= 0 || G > 0x7fffffff) return hipErrorInvalidConfiguration;
     constexpr int lds_bytes = 5 * (256 + BN) * 64;
@@ -1030,7 +1030,7 @@ static hipError_t prepare_gemm_pp64() {
 
 template <int BN, int GM>
 static hipError_t launch_gemm_pp64(const Args &a, int S, hipStream_t st) {
-    if (S != 1 || a.kx != a.K) return hipErrorInvalidValue;  // no K split, no hi/lo pair
+    if (S != 1 || a.kx != a.K || a.wpack) return hipErrorInvalidValue;  // no K split, hi/lo pair or packed W
     const int64_t G = ((a.M + 255) / 256) * ((a.N + BN - 1) / BN);
     if (G <= 0 || G > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((gemm_pp64_kernel<BN, GM>), dim3(static_cast<unsigned>(G)), dim3(512), 5 * 32 * 1024, st, a);
@@ -1056,7 +1056,7 @@ static hipError_t prepare_gemm_pp64p() {
 // S parts of at least two k-ranges each and adds the reduction pass
 template <int BN, int GM>
 static hipError_t launch_gemm_pp64p(const Args &a, int S, hipStream_t st) {
-    if (a.kx != a.K && (a.kx % 64 != 0 || a.K < 128)) return hipErrorInvalidValue;
+    if (a.wpack || (a.kx != a.K && (a.kx % 64 != 0 || a.K < 128))) return hipErrorInvalidValue;
     if (a.K < 128) return S == 1 ? launch_gemm_pp64<BN, GM>(a, 1, st) : hipErrorInvalidValue;
     if (S < 1 || a.K / 64 < 2 * static_cast<int64_t>(S)) return hipErrorInvalidValue;
     const int64_t G = ((a.M + 255) / 256) * ((a.N + BN - 1) / BN) * S;

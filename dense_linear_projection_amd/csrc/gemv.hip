@@ -179,7 +179,7 @@ template <int MR, int R, int WV, int U, int WNT>
 static hipError_t launch_gemv(const Args &a, int S, hipStream_t st) {
     // whole 16-byte chunks, X rows within the variant, offsets within the
     // resources' 31-bit range
-    if (a.K % 8 != 0 || a.kx % 8 != 0 || a.M > MR || S < 1) return hipErrorInvalidValue;
+    if (a.K % 8 != 0 || a.kx % 8 != 0 || a.M > MR || S < 1 || a.wpack) return hipErrorInvalidValue;
     if (static_cast<int64_t>(R) * a.K * 2 > 0x7fffffff || a.M * a.kx * 2 > 0x7fffffff) return hipErrorInvalidValue;
     const int64_t grid = ((a.N + R - 1) / R) * S;
     if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;

@@ -42,6 +42,22 @@ __global__ __launch_bounds__(256) void hilo_split_kernel(const float *W, int64_t
     out[n * 2 * K + K + k] = l;
 }
 
+// W [N][K] row-major -> tiles of R rows, each stored as K/128 consecutive
+// blocks of [R rows][128 columns]; rows past N are zero.  One thread per
+// 16-byte chunk of the packed array.
+__global__ __launch_bounds__(256) void pack_kernel(const uint16_t *W, int64_t N, int64_t K, int R, uint16_t *Wp,
+                                                   int64_t chunks) {
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (idx >= chunks) return;
+    const int64_t per_tile = R * K / 8, per_block = R * 16;
+    const int64_t tile = idx / per_tile, rem = idx % per_tile;
+    const int64_t blk = rem / per_block, in = rem % per_block;
+    const int64_t n = tile * R + in / 16, k = blk * 128 + (in % 16) * 8;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (n < N) v = *reinterpret_cast<const u32x4 *>(W + n * K + k);
+    *reinterpret_cast<u32x4 *>(Wp + idx * 8) = v;
+}
+
 // Reads a large buffer so that the caches hold clean lines of it instead of
 // the next timed kernel's operands (used only while measuring plans).  The
 // loads feed a value that is stored only if it equals a fixed constant, so
@@ -62,6 +78,15 @@ hipError_t launch_flush(const void *buf, size_t bytes, unsigned *sink, hipStream
     return hipGetLastError();
 }
 
+hipError_t launch_pack(const uint16_t *W, int64_t N, int64_t K, int R, uint16_t *Wp, hipStream_t st) {
+    const int64_t tiles = (N + R - 1) / R;
+    const int64_t chunks = tiles * R * K / 8;
+    const int64_t blocks = (chunks + 255) / 256;
+    if (blocks <= 0 || blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(pack_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, W, N, K, R, Wp, chunks);
+    return hipGetLastError();
+}
+
 hipError_t launch_hilo_split(const float *W, int64_t N, int64_t K, uint16_t *out, hipStream_t st) {
     const int64_t blocks = (N * K + 255) / 256;
     if (blocks <= 0 || blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
@@ -70,6 +95,7 @@ hipError_t launch_hilo_split(const float *W, int64_t N, int64_t K, uint16_t *out
 }
 
 hipError_t launch_generic(const Args &a, hipStream_t st) {
+    if (a.wpack) return hipErrorInvalidValue;
     const int64_t cells = a.M * a.N;
     const int64_t blocks = (cells + 255) / 256;
     if (blocks <= 0 || blocks > 0x7fffffff) return hipErrorInvalidConfiguration;

@@ -47,6 +47,10 @@ hipError_t launch_splitk_reduce(const Args &a, int S, hipStream_t st);
 // Any shape, any alignment (generic.hip).
 hipError_t launch_generic(const Args &a, hipStream_t st);
 
+// bf16 weights [N][K] -> tiles of R rows stored as [K/128][R][128] blocks,
+// rows past N zero (generic.hip).
+hipError_t launch_pack(const uint16_t *W, int64_t N, int64_t K, int R, uint16_t *Wp, hipStream_t st);
+
 // fp32 weights [N][K] -> bf16 hi/lo pair [N][2K] (generic.hip).
 hipError_t launch_hilo_split(const float *W, int64_t N, int64_t K, uint16_t *out, hipStream_t st);
 

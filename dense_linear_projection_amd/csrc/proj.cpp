@@ -44,8 +44,10 @@ struct Key {
     int64_t M, N, K;
     int epi, out, aligned;
     int hilo = 0;
+    int wpack = 0;  // packed weights: 16-row units per tile (0: row-major W)
     bool operator<(const Key &o) const {
-        return std::tie(M, N, K, epi, out, aligned, hilo) < std::tie(o.M, o.N, o.K, o.epi, o.out, o.aligned, o.hilo);
+        return std::tie(M, N, K, epi, out, aligned, hilo, wpack) <
+               std::tie(o.M, o.N, o.K, o.epi, o.out, o.aligned, o.hilo, o.wpack);
     }
 };
 
@@ -156,6 +158,29 @@ std::string gemm_name(const GemmVariant &v, int S) {
 // not performance guesses; the measurement picks among them.
 std::vector<Candidate> candidates(const Key &k) {
     std::vector<Candidate> out;
+    if (k.wpack) {
+        // packed weights are read by the streaming kernel's buffer-resource
+        // path only, with the tile height they were packed for
+        const int mt = mt_for(k.M);
+        if (!k.aligned || k.K <= 0 || k.K % 128 != 0 || (mt == 0 && k.M > kStreamMaxM)) return out;
+        for (int i = 0; i < kNumStreamVariants; ++i) {
+            const StreamVariant &v = kStreamVariants[i];
+            if (v.nt != k.wpack || v.kc % 128 != 0 || k.K % v.kc != 0) continue;
+            if (mt > 0 ? v.mt != mt : (v.mt != 4 && v.mt != 8)) continue;
+            const int64_t rows_x = k.M < 16 * v.mt ? k.M : 16 * v.mt;
+            if (rows_x * k.K * 2 >= (int64_t{1} << 32) || int64_t{16} * v.nt * k.K * 2 >= (int64_t{1} << 32)) continue;
+            const int64_t mblocks = (k.M + 16 * v.mt - 1) / (16 * v.mt);
+            const int64_t stages = k.K / v.kc;
+            const int64_t tiles = (k.N + 16 * v.nt - 1) / (16 * v.nt);
+            for (int S : {1, 2, 4, 8, 16}) {
+                if (S > 1 && S > stages) continue;
+                if (S > 1 && static_cast<size_t>(S) * k.M * k.N * sizeof(float) > kWorkspaceBytes) continue;
+                if (mblocks * tiles * S > 0x7fffffff) continue;
+                out.push_back({KIND_STREAM, i, S, stream_name(v, S)});
+            }
+        }
+        return out;
+    }
     if (k.aligned && k.K > 0) {
         // row blocks of the streaming kernel: the one block size that covers
         // M up to 64 rows; above that, 64- or 128-row blocks up to
@@ -255,9 +280,10 @@ Candidate default_candidate(const Key &k) {
 }
 
 Args make_args(proj_ctx *c, const void *X, const void *W, const void *bias, int epi, int64_t M, int64_t N,
-               int64_t K, void *Y, int out, int hilo = 0) {
+               int64_t K, void *Y, int out, int hilo = 0, int wpack = 0) {
     Args a;
     a.kx = hilo ? K / 2 : K;
+    a.wpack = wpack;
     a.X = static_cast<const uint16_t *>(X);
     a.W = static_cast<const uint16_t *>(W);
     a.bias = static_cast<const uint16_t *>(bias);
@@ -324,10 +350,11 @@ proj_status check_args(proj_ctx *c, const void *X, const void *W, const void *bi
     return PROJ_OK;
 }
 
-Key make_key(const void *X, const void *W, int epi, int64_t M, int64_t N, int64_t K, int out, int hilo = 0) {
+Key make_key(const void *X, const void *W, int epi, int64_t M, int64_t N, int64_t K, int out, int hilo = 0,
+             int wpack = 0) {
     const bool al = (reinterpret_cast<uintptr_t>(X) % 16 == 0) && (reinterpret_cast<uintptr_t>(W) % 16 == 0) &&
                     ((hilo ? K / 2 : K) % 8 == 0);
-    return Key{M, N, K, epi, out, al ? 1 : 0, hilo};
+    return Key{M, N, K, epi, out, al ? 1 : 0, hilo, wpack};
 }
 
 bool capturing(hipStream_t st) {
@@ -426,13 +453,18 @@ proj_status tune(proj_ctx *c, const Key &k, const Args &a, hipStream_t st, Plan 
 }
 
 proj_status run_impl(proj_ctx *c, const void *X, const void *W, const void *bias, int epi, int64_t M, int64_t N,
-                     int64_t K, void *Y, int out, void *stream, bool force_tune, int hilo = 0) {
+                     int64_t K, void *Y, int out, void *stream, bool force_tune, int hilo = 0, int wpack = 0) {
     proj_status s = check_args(c, X, W, bias, epi, M, N, K, Y, out);
     if (s != PROJ_OK || M == 0 || N == 0) return s;
     DeviceGuard g(c->device);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const Key k = make_key(X, W, epi, M, N, K, out, hilo);
-    const Args a = make_args(c, X, W, bias, epi, M, N, K, Y, out, hilo);
+    const Key k = make_key(X, W, epi, M, N, K, out, hilo, wpack);
+    const Args a = make_args(c, X, W, bias, epi, M, N, K, Y, out, hilo, wpack);
+    if (wpack && candidates(k).empty()) {
+        set_err(c, "no kernel reads packed weights for M=%lld K=%lld (M <= %lld, K a multiple of 128, "
+                   "16-byte aligned X and W)", (long long)M, (long long)K, (long long)kStreamMaxM);
+        return PROJ_ERR_UNSUPPORTED;
+    }
     const bool cap = capturing(st);
     if (force_tune && cap) {
         set_err(c, "cannot tune while the stream is capturing");
@@ -528,6 +560,51 @@ proj_status proj_run_hilo(proj_ctx *ctx, const void *X, const void *Whl, const v
                           int64_t N, int64_t K, void *Y, int out_dtype, void *stream) {
     if (K < 0 || K > (int64_t(1) << 40)) return PROJ_ERR_INVALID_ARG;
     return run_impl(ctx, X, Whl, bias, epilogue, M, N, 2 * K, Y, out_dtype, stream, false, 1);
+}
+
+// Tile heights (in 16-row units) that some streaming variant reads.
+static bool packable_tile(int t) {
+    for (int i = 0; i < kNumStreamVariants; ++i)
+        if (kStreamVariants[i].nt == t && kStreamVariants[i].kc % 128 == 0) return true;
+    return false;
+}
+
+int64_t proj_packed_bytes(int64_t N, int64_t K, int tile16) {
+    if (N < 0 || K < 0 || K % 128 != 0 || !packable_tile(tile16) || N > (int64_t(1) << 40) / (K > 0 ? K : 1))
+        return -1;
+    const int64_t R = 16 * static_cast<int64_t>(tile16);
+    return ((N + R - 1) / R) * R * K * 2;
+}
+
+proj_status proj_pack_weights(proj_ctx *ctx, const void *W, int64_t N, int64_t K, int tile16, void *Wp,
+                              void *stream) {
+    if (!ctx) return PROJ_ERR_INVALID_ARG;
+    if (ctx->magic == kDead) return PROJ_ERR_DESTROYED;
+    if (ctx->magic != kMagic) return PROJ_ERR_INVALID_ARG;
+    if (proj_packed_bytes(N, K, tile16) < 0) {
+        set_err(ctx, "cannot pack N=%lld K=%lld in tiles of %d x 16 rows (K must be a multiple of 128; "
+                     "tile heights: those of the streaming kernel)", (long long)N, (long long)K, tile16);
+        return PROJ_ERR_INVALID_ARG;
+    }
+    if (N == 0 || K == 0) return PROJ_OK;
+    if (!W || !Wp || reinterpret_cast<uintptr_t>(W) % 16 || reinterpret_cast<uintptr_t>(Wp) % 16) {
+        set_err(ctx, "W or Wp is NULL or not 16-byte aligned");
+        return PROJ_ERR_INVALID_ARG;
+    }
+    DeviceGuard g(ctx->device);
+    hipError_t e = launch_pack(static_cast<const uint16_t *>(W), N, K, 16 * tile16, static_cast<uint16_t *>(Wp),
+                               static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(ctx, "launch", e);
+    return PROJ_OK;
+}
+
+proj_status proj_run_packed(proj_ctx *ctx, const void *X, const void *Wp, int tile16, const void *bias, int epilogue,
+                            int64_t M, int64_t N, int64_t K, void *Y, int out_dtype, void *stream) {
+    if (!packable_tile(tile16)) {
+        if (ctx && ctx->magic == kMagic) set_err(ctx, "no streaming variant reads tiles of %d x 16 rows", tile16);
+        return PROJ_ERR_INVALID_ARG;
+    }
+    return run_impl(ctx, X, Wp, bias, epilogue, M, N, K, Y, out_dtype, stream, false, 0, tile16);
 }
 
 proj_status proj_destroy(proj_ctx *ctx) {
@@ -648,6 +725,45 @@ proj_status proj_run_candidate(proj_ctx *ctx, int index, const void *X, const vo
     }
     DeviceGuard g(ctx->device);
     hipError_t e = launch(c[index], make_args(ctx, X, W, bias, epi, M, N, K, Y, out), static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(ctx, "launch", e);
+    return PROJ_OK;
+}
+
+proj_status proj_get_plan_packed(proj_ctx *ctx, int64_t M, int64_t N, int64_t K, int tile16, int epi, int out,
+                                 int aligned16, char *buf, size_t len) {
+    return get_plan(ctx, Key{M, N, K, epi, out, aligned16 ? 1 : 0, 0, tile16}, buf, len);
+}
+
+int proj_num_candidates_packed(int64_t M, int64_t N, int64_t K, int tile16, int epi, int out, int aligned16) {
+    if (M <= 0 || N <= 0 || K < 0 || !packable_tile(tile16)) return 0;
+    return static_cast<int>(candidates(Key{M, N, K, epi, out, aligned16 ? 1 : 0, 0, tile16}).size());
+}
+
+proj_status proj_candidate_name_packed(int64_t M, int64_t N, int64_t K, int tile16, int epi, int out, int aligned16,
+                                       int index, char *buf, size_t len) {
+    if (M <= 0 || N <= 0 || K < 0 || !buf || !packable_tile(tile16)) return PROJ_ERR_INVALID_ARG;
+    std::vector<Candidate> c = candidates(Key{M, N, K, epi, out, aligned16 ? 1 : 0, 0, tile16});
+    if (index < 0 || index >= static_cast<int>(c.size())) return PROJ_ERR_INVALID_ARG;
+    if (c[index].name.size() + 1 > len) return PROJ_ERR_INVALID_ARG;
+    std::strcpy(buf, c[index].name.c_str());
+    return PROJ_OK;
+}
+
+proj_status proj_run_candidate_packed(proj_ctx *ctx, int index, const void *X, const void *Wp, int tile16,
+                                      const void *bias, int epi, int64_t M, int64_t N, int64_t K, void *Y, int out,
+                                      void *stream) {
+    proj_status s = check_args(ctx, X, Wp, bias, epi, M, N, K, Y, out);
+    if (s != PROJ_OK || M == 0 || N == 0) return s;
+    if (!packable_tile(tile16)) return PROJ_ERR_INVALID_ARG;
+    const Key k = make_key(X, Wp, epi, M, N, K, out, 0, tile16);
+    std::vector<Candidate> c = candidates(k);
+    if (index < 0 || index >= static_cast<int>(c.size())) {
+        set_err(ctx, "candidate %d out of range (%d)", index, static_cast<int>(c.size()));
+        return PROJ_ERR_INVALID_ARG;
+    }
+    DeviceGuard g(ctx->device);
+    hipError_t e = launch(c[index], make_args(ctx, X, Wp, bias, epi, M, N, K, Y, out, 0, tile16),
+                          static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(ctx, "launch", e);
     return PROJ_OK;
 }

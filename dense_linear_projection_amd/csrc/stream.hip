@@ -42,6 +42,11 @@
 // Chunks past K or rows past M / N read the zero page (no load leaves the
 // caller's buffers); rows past M / N are not stored.
 //
+// Packed weights (a.wpack == NT, FAST only): the tile's rows are stored as
+// consecutive blocks of [16*NT rows][128 columns], one per 128-column step
+// of K, so a stage of the tile is one contiguous run of 16*NT*KC*2 bytes
+// instead of 16*NT row pieces 2K bytes apart.  Only the copy offsets change.
+//
 // FAST (chosen per call when K is a multiple of KC): the copies go through
 // buffer resources over the tile's W rows and over X, with the per-lane
 // offsets fixed for the whole loop and the stage's k offset a scalar, so a
@@ -141,16 +146,20 @@ __global__ __launch_bounds__(WAVES * 64) void stream_kernel(Args a, int S) {
     // copy's byte offset within its operand
     uint32_t wbytes = 0, xbytes = 0;
     uint32_t voff[C::PERW];
+    const bool packed = a.wpack != 0;
     if constexpr (FAST) {
-        const int64_t rows_w = (N - n0) < C::NR ? (N - n0) : C::NR;
+        // a packed tile is whole: rows past N are zeros in the packed array
+        const int64_t rows_w = packed ? C::NR : (N - n0) < C::NR ? (N - n0) : C::NR;
         wbytes = static_cast<uint32_t>(rows_w * K * 2);
         xbytes = static_cast<uint32_t>(M * a.kx * 2);
 #pragma unroll
         for (int j = 0; j < C::PERW; ++j) {
             const int row = (wave + j * WAVES) * C::RPI + lane / C::CPR;
             const int chunk = (lane % C::CPR) ^ (row & 15);
-            // W rows are K long, X rows kx long
-            voff[j] = static_cast<uint32_t>(row < C::NR ? (row * K + chunk * 8) * 2 : ((row - C::NR) * a.kx + chunk * 8) * 2);
+            // W rows are K long (packed: chunk c of a row sits in 128-column
+            // block c / 16 of the stage), X rows kx long
+            const int64_t wofs = packed ? (chunk / 16) * C::NR * 128 + row * 128 + (chunk % 16) * 8 : row * K + chunk * 8;
+            voff[j] = static_cast<uint32_t>(row < C::NR ? wofs * 2 : ((row - C::NR) * a.kx + chunk * 8) * 2);
         }
     }
     auto issue = [&](int i) {
@@ -158,7 +167,7 @@ __global__ __launch_bounds__(WAVES * 64) void stream_kernel(Args a, int S) {
         if constexpr (FAST) {
             const bool live = i < nst;
             const int64_t k0 = stage_k0(live ? i : 0);
-            const uint32_t soff = static_cast<uint32_t>(k0 * 2);
+            const uint32_t soff = static_cast<uint32_t>(k0 * 2 * (packed ? C::NR : 1));
             // X column of a hi/lo pair's second half wraps to the start
             const uint32_t soffx = static_cast<uint32_t>((k0 >= a.kx ? k0 - a.kx : k0) * 2);
             const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(a.W + n0 * K, live ? wbytes : 0u);
@@ -326,6 +335,7 @@ static hipError_t launch_stream(const Args &a, int S, hipStream_t st) {
     const bool fast = a.K % KC == 0 && a.kx % KC == 0 && rows_x * a.kx * 2 < (int64_t{1} << 32) &&
                       16 * NT * a.K * 2 < (int64_t{1} << 32);
     if (!fast && a.kx != a.K) return hipErrorInvalidValue;
+    if (a.wpack && (a.wpack != NT || !fast || KC % 128 != 0)) return hipErrorInvalidValue;
     if (fast)
         hipLaunchKernelGGL((stream_kernel<MT, NT, WV, KC, D, WNT, true>), dim3(static_cast<unsigned>(grid)),
                            dim3(WV * 64), lds_bytes, st, a, S);

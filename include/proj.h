@@ -142,6 +142,54 @@ proj_status proj_run_hilo(proj_ctx *ctx, const void *X, const void *Whl, const v
                           int epilogue, int64_t M, int64_t N, int64_t K, void *Y,
                           int out_dtype, void *stream);
 
+/* ---- Registered (packed) bf16 weights (worklog "How I made Muse's GPU
+ * projections 1.32x faster in the Open Kernel Challenge", section "Weight
+ * packing and library descriptors solve related but different problems":
+ * the same bf16 values moved to new addresses once, so that each block reads
+ * its weights as one contiguous run).
+ *
+ * Layout for tile height R = 16 * tile16 rows: W [N][K] row-major becomes
+ * ceil(N / R) tiles, tile t holding rows t*R .. t*R + R - 1 as K/128
+ * consecutive blocks of [R rows][128 columns] (block b holds columns
+ * 128b .. 128b + 127); rows past N are zero.  Element (n, k) sits at
+ * ((n / R) * K/128 + k / 128) * R * 128 + (n % R) * 128 + k % 128.
+ * Values are copied bit for bit.  The streaming kernel then reads a stage of
+ * a tile as one contiguous run instead of R row pieces 2K bytes apart.
+ * tile16 must be a tile height of the streaming kernel (1, 2, 4 or 7) and K
+ * a positive multiple of 128. */
+
+/* Size in bytes of the packed array for (N, K, tile16), or -1 if that
+ * packing is not offered. */
+int64_t proj_packed_bytes(int64_t N, int64_t K, int tile16);
+
+/* Pack bf16 W [N][K] (device, row-major) into the caller-allocated device
+ * array Wp of proj_packed_bytes(N, K, tile16) bytes, enqueued on `stream`.
+ * W and Wp stay owned by the caller and must not overlap.  N = 0 or K = 0 is
+ * a no-op; invalid sizes, tile heights, NULL or non-16-byte-aligned
+ * pointers give PROJ_ERR_INVALID_ARG. */
+proj_status proj_pack_weights(proj_ctx *ctx, const void *W, int64_t N, int64_t K, int tile16, void *Wp,
+                              void *stream);
+
+/* Y = epilogue(X W^T (+ bias)) with W given packed (Wp, tile16 as packed).
+ * Arguments, output and capture rules as proj_run.  The plan is measured
+ * per shape among the streaming kernel's variants of that tile height
+ * (row blocks and K splits included); PROJ_ERR_UNSUPPORTED where none
+ * applies (M above 512, unaligned X or Wp). */
+proj_status proj_run_packed(proj_ctx *ctx, const void *X, const void *Wp, int tile16, const void *bias,
+                            int epilogue, int64_t M, int64_t N, int64_t K, void *Y, int out_dtype,
+                            void *stream);
+
+/* Introspection for packed weights, as for proj_run. */
+proj_status proj_get_plan_packed(proj_ctx *ctx, int64_t M, int64_t N, int64_t K, int tile16, int epilogue,
+                                 int out_dtype, int aligned16, char *buf, size_t buflen);
+int proj_num_candidates_packed(int64_t M, int64_t N, int64_t K, int tile16, int epilogue, int out_dtype,
+                               int aligned16);
+proj_status proj_candidate_name_packed(int64_t M, int64_t N, int64_t K, int tile16, int epilogue,
+                                       int out_dtype, int aligned16, int index, char *buf, size_t buflen);
+proj_status proj_run_candidate_packed(proj_ctx *ctx, int index, const void *X, const void *Wp, int tile16,
+                                      const void *bias, int epilogue, int64_t M, int64_t N, int64_t K,
+                                      void *Y, int out_dtype, void *stream);
+
 /* Free the context (synchronises its device first).  The handle must not be
  * used afterwards; a second destroy of the same pointer is undefined. */
 proj_status proj_destroy(proj_ctx *ctx);

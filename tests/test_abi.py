@@ -78,3 +78,28 @@ def test_create_without_gpu_fails_cleanly():
     with pytest.raises(dlp.ProjError) as e:
         dlp.proj_create(0)
     assert e.value.status in (dlp.PROJ_ERR_HIP, dlp.PROJ_ERR_INVALID_ARG)
+
+
+def test_packed_layout_host_rules():
+    """Packed-weight sizes and candidate lists are host logic: tiles of
+    16 * tile16 rows padded with zero rows, K a multiple of 128, only the
+    streaming kernel's tile heights, and no plan above 512 token rows."""
+    assert dlp.proj_packed_bytes(100, 256, 1) == 7 * 16 * 256 * 2
+    assert dlp.proj_packed_bytes(100, 256, 7) == 1 * 112 * 256 * 2
+    assert dlp.proj_packed_bytes(8192, 8192, 2) == 8192 * 8192 * 2
+    assert dlp.proj_packed_bytes(0, 256, 2) == 0
+    assert dlp.proj_packed_bytes(100, 200, 2) == -1      # K not a multiple of 128
+    assert dlp.proj_packed_bytes(100, 256, 3) == -1      # no streaming tile of 48 rows
+    assert dlp.proj_packed_bytes(-1, 256, 2) == -1
+    n = dlp.proj_num_candidates_packed(16, 8192, 8192, 2, dlp.EPI_BIAS, dlp.OUT_BF16)
+    names = [dlp.proj_candidate_name_packed(16, 8192, 8192, 2, dlp.EPI_BIAS, dlp.OUT_BF16, i) for i in range(n)]
+    assert n > 0 and all(x.startswith("stream_mt1_nt2_") for x in names)
+    assert dlp.proj_num_candidates_packed(513, 8192, 8192, 2, 0, 0) == 0
+    assert dlp.proj_num_candidates_packed(16, 8192, 8192, 3, 0, 0) == 0
+    assert dlp.proj_num_candidates_packed(16, 8192, 8200, 2, 0, 0) == 0
+    assert dlp.proj_num_candidates_packed(16, 8192, 8192, 2, 0, 0, aligned16=False) == 0
+    # 384 = 3 x 128: the 256-column stage variants are not offered
+    names = [dlp.proj_candidate_name_packed(200, 300, 384, 4, 0, 0, i)
+             for i in range(dlp.proj_num_candidates_packed(200, 300, 384, 4, 0, 0))]
+    assert names and not any("_k256_" in x for x in names)
+    assert all(re.match(r"stream_mt(4|8)_nt4_", x) for x in names)
