@@ -56,7 +56,7 @@ enum Kind { KIND_STREAM = 0, KIND_GEMM = 1, KIND_GENERIC = 2, KIND_GEMV = 3 };
 struct Candidate {
     Kind kind;
     int variant;  // index into the kernel table
-    int splits;   // stream only: K ranges over workgroups
+    int splits;   // K ranges over workgroups (1: no split)
     std::string name;
 };
 

@@ -30,7 +30,10 @@
  * that gives results within the same tolerance.
  *
  * Streams: `stream` is a hipStream_t passed as void* (NULL = the legacy
- * default stream).  proj_run only enqueues work and returns; it never
+ * default stream).  Once a shape's plan is chosen (the first uncaptured call
+ * for a shape measures the candidate plans, synchronising the stream and
+ * possibly allocating a 512 MiB buffer used to flush caches while timing;
+ * see proj_run), proj_run only enqueues work and returns: it never
  * synchronises, allocates or reads device memory on the host, so it may be
  * recorded into a HIP graph (stream capture) -- see "Capture" below.
  *
@@ -91,6 +94,12 @@ proj_status proj_create(proj_ctx **ctx, int device);
  * proj_epilogue, `out_dtype` a proj_out_dtype; unknown values give
  * PROJ_ERR_INVALID_ARG, as do NULL X/W/Y (when the sizes need them) and a
  * bias epilogue with bias == NULL.
+ *
+ * Kernel families: a register-streaming GEMV (M <= 8), an LDS-staged
+ * weight-streaming kernel with MFMA (M <= 64, and up to 512 in row blocks),
+ * MFMA GEMMs (any M, K a multiple of 32 or 64), and an any-shape kernel;
+ * K may be split over workgroups, with a second kernel adding the fp32
+ * partials in split order and applying the epilogue.
  *
  * Plan choice (kernel family, tile shape, split count): on the first call
  * for a shape key (M, N, K, epilogue, out dtype, alignment) outside stream

@@ -41,7 +41,8 @@ def test_replay_follows_fresh_input(ctx):
         dlp.proj_graph_destroy(g)
 
 
-@pytest.mark.parametrize("shape", [(16, 1024, 8192), (16, 8192, 1024), (300, 640, 512)])
+@pytest.mark.parametrize("shape", [(16, 1024, 8192), (16, 8192, 1024), (300, 640, 512),
+                                   (1, 2304, 8192), (8, 1024, 4096), (130, 512, 1024)])
 def test_graph_replays_match_oracle(ctx, shape):
     """Capture several calls over rotating buffers; replay with eager work
     and synchronisations in between, new X each time; check every replay."""

@@ -119,3 +119,39 @@ def test_packed_errors(ctx):
         dlp.proj_run_packed(ctx, X[:16], Wp, 3, None, dlp.EPI_NONE, out_tensor(16, 64, oracle.OUT_F32), 64)
     with pytest.raises(ValueError):                 # K not a multiple of 128
         dlp.proj_pack_weights(ctx, dev_bf16(synth.integer_bf16((8, 200), -2, 2, 3)), 1)
+
+
+def test_packed_graph_replays(ctx):
+    """The tuned packed plan captured in a torch CUDA graph over two buffer
+    sets; every replay, with new X and eager work in between, matches the
+    oracle."""
+    M, N, K, tile16 = 16, 2048, 4096, 2
+    Ws = [synth.normal_bf16((N, K), 1.0 / np.sqrt(K), 90 + p) for p in range(2)]
+    bs = [synth.normal_bf16((N,), 0.14, 92 + p) for p in range(2)]
+    Wps = [dlp.proj_pack_weights(ctx, dev_bf16(w), tile16) for w in Ws]
+    bd = [dev_bf16(b) for b in bs]
+    Xd = [dev_bf16(synth.normal_bf16((M, K), 1.0, 94 + p)) for p in range(2)]
+    Ys = [out_tensor(M, N, oracle.OUT_BF16) for _ in range(2)]
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        for p in range(2):
+            dlp.proj_run_packed(ctx, Xd[p], Wps[p], tile16, bd[p], dlp.EPI_BIAS, Ys[p], N, stream=s)
+        s.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for p in range(2):
+                dlp.proj_run_packed(ctx, Xd[p], Wps[p], tile16, bd[p], dlp.EPI_BIAS, Ys[p], N, stream=s)
+    for rep in range(3):
+        Xs = [synth.normal_bf16((M, K), 1.0, 500 + 10 * rep + p) for p in range(2)]
+        for p in range(2):
+            Xd[p].copy_(dev_bf16(Xs[p]))
+        junk = torch.randn(1 << 20, device="cuda").sum()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            g.replay()
+        s.synchronize()
+        del junk
+        for p in range(2):
+            r, _ = oracle.reference(Xs[p], Ws[p], bs[p], oracle.EPI_BIAS, oracle.OUT_BF16)
+            rep_ = compare.check(host_f64(Ys[p]), r)
+            assert rep_["ok"], (rep, p, rep_)
