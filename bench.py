@@ -434,6 +434,49 @@ def time_packed(ctx, w, args, Xs, Ws, bs, Ys, idx, stream) -> dict:
             "note": "W packed once before timing (registration); five trials of the same steps, median"}
 
 
+def run_candidate(args) -> int:
+    """Run one candidate plan of a workload args.reps times over two
+    buffer sets (no tuning), for rocprofv3 counter passes."""
+    import numpy as np
+    import torch
+
+    import dense_linear_projection_amd as dlp
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    to_dev = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    names = [dlp.proj_candidate_name(w.M, w.N, w.K, w.epi, w.out_dtype, i)
+             for i in range(dlp.proj_num_candidates(w.M, w.N, w.K, w.epi, w.out_dtype))]
+    hits = [i for i, n in enumerate(names) if args.candidate in n]
+    if not hits:
+        print("no candidate contains %r" % args.candidate, file=sys.stderr)
+        return 2
+    i = hits[0]
+    sets = []
+    for p in range(2):
+        X, W, b = synth.workload_inputs(w, offset=100 * p)
+        out_t = torch.float32 if w.out_dtype == synth.OUT_F32 else torch.bfloat16
+        sets.append((to_dev(X), to_dev(W), to_dev(b) if b is not None else None,
+                     torch.empty((w.M, w.N), dtype=out_t, device=dev)))
+    ctx = dlp.proj_create(0)
+    stream = torch.cuda.Stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for r in range(args.reps):
+            Xd, Wd, bd, Y = sets[r % 2]
+            dlp.proj_run_candidate(ctx, i, Xd, Wd, bd, w.epi, Y, stream=stream)
+        e1.record(stream)
+    e1.synchronize()
+    dlp.proj_destroy(ctx)
+    print(json.dumps({"workload": w.name, "candidate": names[i], "reps": args.reps,
+                      "mean_us": round(e0.elapsed_time(e1) * 1e3 / args.reps, 3)}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -454,6 +497,10 @@ def main() -> int:
                     help="also time the path with W registered in the packed tile layout of 16*TILE16 rows "
                          "(packing outside the timed region; reported beside the row-major figure). "
                          "-1: the tile height of the row-major plan, for weight-streaming workloads; 0: off")
+    ap.add_argument("--candidate", default="",
+                    help="run the first candidate plan whose name contains this text --reps times on the "
+                         "workload (for hardware counters; prints only its name and mean time)")
+    ap.add_argument("--reps", type=int, default=12, help="runs for --candidate")
     ap.add_argument("--plans", nargs="+", default=[],
                     help="for --ingest: one-pass stream plans to take counters for")
     args = ap.parse_args()
@@ -463,6 +510,8 @@ def main() -> int:
         return copy_calibration()
     if args.sweep:
         return sweep(args)
+    if args.candidate:
+        return run_candidate(args)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the projection path is single-GPU in this build "
@@ -622,6 +671,11 @@ def main() -> int:
     }
     if packed is not None:
         line["packed_weights"] = packed
+    props = torch.cuda.get_device_properties(0)
+    line["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                      "compute_units": props.multi_processor_count,
+                      "peaks_used": {"hbm_gbs": HBM_PEAK_GBS, "bf16_mfma_tflops": BF16_PEAK_TFLOPS},
+                      "note": "peaks are the published MI355X figures (2.4 GHz); the sustained clock under load is lower"}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, X, W, b, args.cpu_seconds)
     else:
