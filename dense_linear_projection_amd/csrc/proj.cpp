@@ -71,6 +71,7 @@ struct Plan {
 struct proj_ctx {
     uint32_t magic;
     int device;
+    int cus;  // compute units of the device
     float *ws;
     uint16_t *zeros;
     void *flush;
@@ -363,6 +364,49 @@ bool capturing(hipStream_t st) {
     return s != hipStreamCaptureStatusNone;
 }
 
+// Workgroups of a candidate's main kernel, and the M x N extent its matrix
+// operations actually cover (whole tiles, padded past M and N).
+struct Extent {
+    int64_t wgs, mp, np;
+};
+Extent candidate_extent(const Candidate &c, const Key &k) {
+    auto up = [](int64_t x, int64_t t) { return (x + t - 1) / t * t; };
+    switch (c.kind) {
+        case KIND_STREAM: {
+            const StreamVariant &v = kStreamVariants[c.variant];
+            const int64_t mp = up(k.M, 16 * v.mt), np = up(k.N, 16 * v.nt);
+            return {mp / (16 * v.mt) * (np / (16 * v.nt)) * c.splits, mp, np};
+        }
+        case KIND_GEMV: {
+            const GemvVariant &v = kGemvVariants[c.variant];
+            const int64_t np = up(k.N, v.rows);
+            return {np / v.rows * c.splits, static_cast<int64_t>(v.mr), np};
+        }
+        case KIND_GEMM: {
+            const GemmVariant &v = kGemmVariants[c.variant];
+            const int64_t mp = up(k.M, v.bm), np = up(k.N, v.bn);
+            return {mp / v.bm * (np / v.bn) * c.splits, mp, np};
+        }
+        default:
+            return {(k.M * k.N + 255) / 256, k.M, k.N};
+    }
+}
+
+// A time no run of the candidate can beat: the multiply-adds its tiles
+// cover (2 Mp Np K) at one CU's share of the published dense bf16 matrix
+// peak (2.5 PFLOP/s over 256 CUs) on each CU it occupies.  The tuner does not
+// launch candidates whose bound is far above the best time already measured
+// (a 256-row GEMM tile walking a very long K for 16 token rows alone would
+// take milliseconds to seconds).
+double lower_bound_us(const Candidate &c, const Key &k, int cus) {
+    const Extent e = candidate_extent(c, k);
+    const double wgs = std::max<double>(1.0, std::min<double>(static_cast<double>(e.wgs), cus));
+    const double per_cu = 2.5e15 / 256.0;
+    return 2.0 * static_cast<double>(e.mp) * static_cast<double>(e.np) * static_cast<double>(k.K) / (wgs * per_cu) *
+           1e6;
+}
+constexpr double kSkipFactor = 20.0;
+
 // Time every candidate on the caller's buffers; returns the winner.  The
 // last-level cache is flushed before each timed run when the operands could
 // fit in it, so small shapes are timed as they run from HBM.
@@ -395,9 +439,12 @@ proj_status tune(proj_ctx *c, const Key &k, const Args &a, hipStream_t st, Plan 
         std::sort(t.begin(), t.end());
         return t[t.size() / 2];
     };
-    // pass 1: every candidate, a few runs each
+    // pass 1: every candidate, a few runs each (except those whose lower
+    // bound is already far behind the best median so far)
     std::vector<std::pair<float, size_t>> ranked;
+    float best_so_far = -1.f;
     for (size_t i = 0; i < cands.size(); ++i) {
+        if (best_so_far > 0.f && lower_bound_us(cands[i], k, c->cus) > kSkipFactor * best_so_far) continue;
         if (launch(cands[i], a, st) != hipSuccess) {  // warm-up; skip variants that cannot launch
             (void)hipGetLastError();
             continue;
@@ -413,6 +460,7 @@ proj_status tune(proj_ctx *c, const Key &k, const Args &a, hipStream_t st, Plan 
             continue;
         }
         ranked.push_back({median(t), i});
+        if (best_so_far < 0.f || ranked.back().first < best_so_far) best_so_far = ranked.back().first;
     }
     if (ranked.empty()) {
         hipEventDestroy(e0);
@@ -508,6 +556,7 @@ proj_status proj_create(proj_ctx **out, int device) {
     if (!c) return PROJ_ERR_NO_MEMORY;
     c->magic = kMagic;
     c->device = device;
+    c->cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
     c->ws = nullptr;
     c->zeros = nullptr;
     c->flush = nullptr;

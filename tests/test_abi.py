@@ -103,3 +103,17 @@ def test_packed_layout_host_rules():
              for i in range(dlp.proj_num_candidates_packed(200, 300, 384, 4, 0, 0))]
     assert names and not any("_k256_" in x for x in names)
     assert all(re.match(r"stream_mt(4|8)_nt4_", x) for x in names)
+
+
+def test_offset_limits_in_candidate_lists():
+    """Variants whose buffer-resource offsets would pass 32 (GEMV: 31) bits
+    are not offered: at K = 2^26 a packed 32-row tile spans 2^32 bytes and a
+    16-row GEMV workgroup 2^31 bytes."""
+    K = 1 << 26
+    assert dlp.proj_num_candidates_packed(16, 1024, K, 2, 0, 0) == 0
+    assert dlp.proj_num_candidates_packed(16, 1024, K, 1, 0, 0) > 0
+    n = dlp.proj_num_candidates(1, 1024, K, 0, 0)
+    gemv = [x for x in (dlp.proj_candidate_name(1, 1024, K, 0, 0, i) for i in range(n)) if x.startswith("gemv")]
+    assert gemv and not any("_r16_" in x for x in gemv)
+    n = dlp.proj_num_candidates(1, 1024, 1 << 20, 0, 0)
+    assert any("_r16_" in dlp.proj_candidate_name(1, 1024, 1 << 20, 0, 0, i) for i in range(n))
