@@ -308,8 +308,17 @@ hipError_t launch(const Candidate &cand, const Args &a, hipStream_t st) {
     }
 }
 
+// Whether byte ranges [a, a + na) and [b, b + nb) share a byte.
+bool overlap(const void *a, uint64_t na, const void *b, uint64_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return pa < pb + nb && pb < pa + na;
+}
+
+// K is the product depth (twice the X row length for a hi/lo pair); wpack
+// the packed weights' tile height (0: row-major W).
 proj_status check_args(proj_ctx *c, const void *X, const void *W, const void *bias, int epi, int64_t M,
-                       int64_t N, int64_t K, void *Y, int out) {
+                       int64_t N, int64_t K, void *Y, int out, int hilo = 0, int wpack = 0) {
     if (!c) return PROJ_ERR_INVALID_ARG;
     if (c->magic == kDead) return PROJ_ERR_DESTROYED;
     if (c->magic != kMagic) return PROJ_ERR_INVALID_ARG;
@@ -347,6 +356,19 @@ proj_status check_args(proj_ctx *c, const void *X, const void *W, const void *bi
     if (M > (int64_t(1) << 40) / (N > 0 ? N : 1)) {
         set_err(c, "M*N too large");
         return PROJ_ERR_UNSUPPORTED;
+    }
+    // Y is written (several times while a plan is measured), so it must not
+    // share memory with an input
+    if (K <= (int64_t(1) << 40) / (M > N ? M : N)) {
+        const uint64_t ybytes = static_cast<uint64_t>(M) * N * (out == PROJ_OUT_F32 ? 4 : 2);
+        const uint64_t xbytes = static_cast<uint64_t>(M) * (hilo ? K / 2 : K) * 2;
+        const int64_t pb = wpack ? proj_packed_bytes(N, K, wpack) : -1;
+        const uint64_t wbytes = pb >= 0 ? static_cast<uint64_t>(pb) : static_cast<uint64_t>(N) * K * 2;
+        const uint64_t bbytes = (epi & 1) ? static_cast<uint64_t>(N) * 2 : 0;
+        if (overlap(Y, ybytes, X, xbytes) || overlap(Y, ybytes, W, wbytes) || overlap(Y, ybytes, bias, bbytes)) {
+            set_err(c, "Y overlaps X, W or bias");
+            return PROJ_ERR_INVALID_ARG;
+        }
     }
     return PROJ_OK;
 }
@@ -502,7 +524,7 @@ proj_status tune(proj_ctx *c, const Key &k, const Args &a, hipStream_t st, Plan 
 
 proj_status run_impl(proj_ctx *c, const void *X, const void *W, const void *bias, int epi, int64_t M, int64_t N,
                      int64_t K, void *Y, int out, void *stream, bool force_tune, int hilo = 0, int wpack = 0) {
-    proj_status s = check_args(c, X, W, bias, epi, M, N, K, Y, out);
+    proj_status s = check_args(c, X, W, bias, epi, M, N, K, Y, out, hilo, wpack);
     if (s != PROJ_OK || M == 0 || N == 0) return s;
     DeviceGuard g(c->device);
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -737,7 +759,7 @@ proj_status proj_candidate_name_hilo(int64_t M, int64_t N, int64_t K, int epi, i
 
 proj_status proj_run_candidate_hilo(proj_ctx *ctx, int index, const void *X, const void *Whl, const void *bias,
                                     int epi, int64_t M, int64_t N, int64_t K, void *Y, int out, void *stream) {
-    proj_status s = check_args(ctx, X, Whl, bias, epi, M, N, 2 * K, Y, out);
+    proj_status s = check_args(ctx, X, Whl, bias, epi, M, N, 2 * K, Y, out, 1);
     if (s != PROJ_OK || M == 0 || N == 0) return s;
     const Key k = make_key(X, Whl, epi, M, N, 2 * K, out, 1);
     std::vector<Candidate> c = candidates(k);
@@ -801,7 +823,7 @@ proj_status proj_candidate_name_packed(int64_t M, int64_t N, int64_t K, int tile
 proj_status proj_run_candidate_packed(proj_ctx *ctx, int index, const void *X, const void *Wp, int tile16,
                                       const void *bias, int epi, int64_t M, int64_t N, int64_t K, void *Y, int out,
                                       void *stream) {
-    proj_status s = check_args(ctx, X, Wp, bias, epi, M, N, K, Y, out);
+    proj_status s = check_args(ctx, X, Wp, bias, epi, M, N, K, Y, out, 0, tile16);
     if (s != PROJ_OK || M == 0 || N == 0) return s;
     if (!packable_tile(tile16)) return PROJ_ERR_INVALID_ARG;
     const Key k = make_key(X, Wp, epi, M, N, K, out, 0, tile16);

@@ -25,6 +25,7 @@
  *   Y    fp32 or bf16 [M, N]                 (element m*N + n)
  * Pointers are device pointers (hipMalloc'ed or torch CUDA tensors); the
  * caller owns every buffer and keeps it alive until the enqueued work ends.
+ * Y must not share memory with X, W or bias (PROJ_ERR_INVALID_ARG).
  * X/W/bias may be any alignment; the fast kernels need X and W 16-byte
  * aligned and K a multiple of 8, and other cases run a slower generic kernel
  * that gives results within the same tolerance.

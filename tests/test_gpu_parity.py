@@ -197,6 +197,7 @@ def test_degenerate_sizes(ctx):
 
 
 def test_invalid_arguments_are_rejected(ctx):
+    import torch
     W = dev_bf16(synth.normal_bf16((4, 32), 1.0, 1))
     X = dev_bf16(synth.normal_bf16((2, 32), 1.0, 2))
     Y = out_tensor(2, 4, oracle.OUT_F32)
@@ -210,6 +211,17 @@ def test_invalid_arguments_are_rejected(ctx):
     assert L.proj_run(*args(Yp=None)) == dlp.PROJ_ERR_INVALID_ARG
     assert L.proj_run(*args(Yp=Y.data_ptr() + 2)) == dlp.PROJ_ERR_INVALID_ARG  # fp32 Y misaligned
     assert b"bias" in L.proj_last_error(ctx) or L.proj_last_error(ctx)
+    # Y sharing memory with an input (the plan measurement writes Y repeatedly)
+    assert L.proj_run(*args(Yp=X.data_ptr())) == dlp.PROJ_ERR_INVALID_ARG
+    assert b"overlaps" in L.proj_last_error(ctx)
+    assert L.proj_run(*args(Yp=W.data_ptr() + 64)) == dlp.PROJ_ERR_INVALID_ARG
+    b = dev_bf16(synth.normal_bf16((4,), 1.0, 3))
+    assert L.proj_run(*args(epi=1, bias=b.data_ptr(), Yp=b.data_ptr())) == dlp.PROJ_ERR_INVALID_ARG
+    big = torch.zeros(4096, dtype=torch.float32, device="cuda")   # disjoint halves of one allocation
+    Xb = big[:32].view(torch.bfloat16)                              # 2 x 32 bf16 in the first 128 bytes
+    assert L.proj_run(ctx, Xb.data_ptr(), W.data_ptr(), None, 0, 2, 4, 32, big[1024:].data_ptr(), 0,
+                      None) == dlp.PROJ_OK
+    torch.cuda.synchronize()
 
 
 def test_nonfinite_inputs_propagate(ctx):
