@@ -16,6 +16,13 @@ taken as the timed region divided by K (this includes the small gaps between
 graph nodes, so it is an upper bound on the kernel's own duration).
 
 Prints ONE JSON line.  Default workload: M=16 K=8192 N=8192, bias, bf16 out.
+Beside the row-major figure the line carries the same steps with W
+registered in the packed tile layout (`packed_weights`), five repeat trials,
+a cache-resident (warm) figure, the oracle's CPU rate and the device.
+
+Other modes: --sweep (the thirty-shape set, torch timed alongside),
+--candidate NAME (one plan repeated, for counter passes), --copy-calibration
+and --ingest (scaling and storing rocprofv3 traffic counters).
 """
 from __future__ import annotations
 
