@@ -197,6 +197,15 @@ def cpu_baseline(w, X, W, b, min_seconds: float):
             break
     frac = rows / w.M
     bytes_done = w.alg_bytes() * frac * reps
+    # one thread, on one row of Y (all N columns, full K), three runs: median
+    t1 = []
+    for _ in range(3):
+        t = time.perf_counter()
+        oracle.proj_f64(np.ascontiguousarray(X[:1]), W, b, w.epi, nthreads=1)
+        t1.append(time.perf_counter() - t)
+    t1.sort()
+    one = {"gflops": round(2 * w.N * w.K / t1[1] / 1e9, 3), "seconds_per_row": round(t1[1], 4),
+           "sample": "1 row of Y, median of 3"}
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -213,6 +222,7 @@ def cpu_baseline(w, X, W, b, min_seconds: float):
         "kind": "oracle",
         "sample": "%d of %d rows of Y (all N columns, full K), %d repetition(s), %.1f s, fp64 C oracle"
                   % (rows, w.M, reps, el),
+        "single_thread": one,
     }
 
 
