@@ -689,8 +689,14 @@ proj_status proj_destroy(proj_ctx *ctx) {
         hipFree(ctx->zeros);
         if (ctx->flush) hipFree(ctx->flush);
     }
+    // the struct itself stays allocated as a marker, so a later use or a
+    // second destroy of this handle reads valid memory and is reported
+    std::lock_guard<std::mutex> lock(ctx->mu);
+    ctx->ws = nullptr;
+    ctx->zeros = nullptr;
+    ctx->flush = nullptr;
+    std::map<Key, Plan>().swap(ctx->plans);
     ctx->magic = kDead;
-    delete ctx;
     return PROJ_OK;
 }
 
@@ -713,6 +719,7 @@ const char *proj_last_error(const proj_ctx *ctx) {
 }
 
 static proj_status get_plan(proj_ctx *ctx, const Key &key, char *buf, size_t len) {
+    if (ctx && ctx->magic == kDead) return PROJ_ERR_DESTROYED;
     if (!ctx || ctx->magic != kMagic || !buf || len == 0) return PROJ_ERR_INVALID_ARG;
     std::lock_guard<std::mutex> lock(ctx->mu);
     auto it = ctx->plans.find(key);
@@ -905,8 +912,10 @@ proj_status proj_graph_destroy(proj_graph *g) {
     DeviceGuard dg(g->device);
     hipGraphExecDestroy(g->exec);
     hipGraphDestroy(g->graph);
+    // kept allocated as a marker (see proj_destroy)
+    g->exec = nullptr;
+    g->graph = nullptr;
     g->magic = kDead;
-    delete g;
     return PROJ_OK;
 }
 

@@ -200,8 +200,10 @@ proj_status proj_run_candidate_packed(proj_ctx *ctx, int index, const void *X, c
                                       const void *bias, int epilogue, int64_t M, int64_t N, int64_t K,
                                       void *Y, int out_dtype, void *stream);
 
-/* Free the context (synchronises its device first).  The handle must not be
- * used afterwards; a second destroy of the same pointer is undefined. */
+/* Free the context's device memory and plans (synchronises its device
+ * first).  The handle itself stays allocated (a few hundred bytes) as a
+ * marker: any later call with it, a second destroy included, returns
+ * PROJ_ERR_DESTROYED. */
 proj_status proj_destroy(proj_ctx *ctx);
 
 /* Static text for a status code (never NULL). */
@@ -262,7 +264,9 @@ proj_status proj_graph_capture(proj_ctx *ctx, int n_calls, const void *const *X,
 /* Enqueue one replay of the graph on `stream`. */
 proj_status proj_graph_launch(proj_graph *graph, void *stream);
 
-/* Free the graph (does not synchronise; the caller waits for replays). */
+/* Free the graph (does not synchronise; the caller waits for replays).  As
+ * with contexts, the handle stays allocated as a marker and later calls with
+ * it return PROJ_ERR_DESTROYED. */
 proj_status proj_graph_destroy(proj_graph *graph);
 
 #ifdef __cplusplus

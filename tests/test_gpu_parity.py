@@ -8,6 +8,8 @@ element by element.
 * every candidate plan of a shape is run (not only the tuned winner), at
   sizes that span several tiles and a ragged tail.
 """
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -237,3 +239,28 @@ def test_nonfinite_inputs_propagate(ctx):
     assert (~np.isfinite(u[5])).all()
     others = [m for m in range(M) if m not in (3, 5)]
     assert np.isfinite(u[others]).all()
+
+
+def test_destroyed_handles_are_reported():
+    """A destroyed context or graph keeps a marker, so using it again, or
+    destroying it a second time, returns PROJ_ERR_DESTROYED."""
+    import torch
+    L = dlp.lib()
+    c = dlp.proj_create(0)
+    X = dev_bf16(synth.normal_bf16((2, 32), 1.0, 4))
+    W = dev_bf16(synth.normal_bf16((4, 32), 1.0, 5))
+    Y = out_tensor(2, 4, oracle.OUT_F32)
+    s = torch.cuda.Stream()
+    g = dlp.proj_graph_capture(c, [X], [W], None, [Y], dlp.EPI_NONE, stream=s)
+    dlp.proj_graph_launch(g, stream=s)
+    s.synchronize()
+    assert L.proj_graph_destroy(g) == dlp.PROJ_OK
+    assert L.proj_graph_destroy(g) == dlp.PROJ_ERR_DESTROYED
+    assert L.proj_graph_launch(g, None) == dlp.PROJ_ERR_DESTROYED
+    assert L.proj_destroy(c) == dlp.PROJ_OK
+    assert L.proj_destroy(c) == dlp.PROJ_ERR_DESTROYED
+    assert L.proj_run(c, X.data_ptr(), W.data_ptr(), None, 0, 2, 4, 32, Y.data_ptr(), 0, None) == \
+        dlp.PROJ_ERR_DESTROYED
+    buf = ctypes.create_string_buffer(64)
+    assert L.proj_get_plan(c, 2, 4, 32, 0, 0, 1, buf, 64) == dlp.PROJ_ERR_DESTROYED
+    assert L.proj_last_error(c) == b""
