@@ -531,7 +531,7 @@ def main() -> int:
         return run_candidate(args)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the projection path is single-GPU in this build "
+        print("bench.py measures one GPU: the projection path runs on a single GPU "
               "(sharding across GPUs is designed, not built). Run with --gpus 1.", file=sys.stderr)
         return 2
 
