@@ -451,6 +451,43 @@ def time_packed(ctx, w, args, Xs, Ws, bs, Ys, idx, stream) -> dict:
             "note": "W packed once before timing (registration); five trials of the same steps, median"}
 
 
+def time_read_floor(ctx, Ws, idx, stream, args) -> dict:
+    """A plain streaming read of the same weight buffers, in the same
+    rotation, captured and replayed the same way as the projection: the
+    measured floor the weight-streaming kernel is compared with."""
+    import torch
+
+    import dense_linear_projection_amd as dlp
+
+    R = len(idx)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in idx:
+            dlp.proj_read_probe(ctx, Ws[i], stream=stream)
+    reps = max(1, args.steps // R)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        g.replay()
+        stream.synchronize()
+        trial_us = []
+        for _ in range(5):
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+            e1.synchronize()
+            trial_us.append(e0.elapsed_time(e1) * 1e3 / (reps * R))
+    del g
+    trial_us.sort()
+    us = trial_us[len(trial_us) // 2]
+    nbytes = Ws[0].numel() * Ws[0].element_size()
+    return {"kernel": "read_probe_kernel", "bytes": nbytes, "median_us": round(us, 3),
+            "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "note": "plain streaming read of each W buffer (contiguous slabs, non-temporal 16-byte loads), "
+                    "same rotation and graph replay as the projection"}
+
+
 def run_candidate(args) -> int:
     """Run one candidate plan of a workload args.reps times over two
     buffer sets (no tuning), for rocprofv3 counter passes."""
@@ -653,6 +690,11 @@ def main() -> int:
             "note": "one buffer set (P=1): operands resident in the 256 MiB last-level cache, not an HBM rate"}
     dlp.proj_graph_destroy(g_warm)
 
+    read_floor = None
+    if hbm_bound:
+        read_floor = time_read_floor(ctx, Ws, idx, stream, args)
+        read_floor["projection_over_floor"] = round(gbs / read_floor["gbs"], 4)
+
     packed = None
     if args.packed < 0 and plan.startswith("stream_"):
         args.packed = int(plan.split("_nt")[1].split("_")[0])
@@ -686,6 +728,8 @@ def main() -> int:
         "trials": trials,
         "warm": warm,
     }
+    if read_floor is not None:
+        line["read_floor"] = read_floor
     if packed is not None:
         line["packed_weights"] = packed
     props = torch.cuda.get_device_properties(0)

@@ -17,7 +17,8 @@ for fp32 weights held as a bf16 high/low pair ``proj_prepare_hilo``,
 weights registered in the packed tile layout ``proj_packed_bytes``,
 ``proj_pack_weights``, ``proj_run_packed``, ``proj_get_plan_packed``,
 ``proj_num_candidates_packed``, ``proj_candidate_name_packed``,
-``proj_run_candidate_packed``.
+``proj_run_candidate_packed``, and the measured read floor
+``proj_read_probe``.
 """
 from __future__ import annotations
 
@@ -44,7 +45,7 @@ EXPORTS = ["proj_create", "proj_run", "proj_tune", "proj_destroy", "proj_status_
            "proj_prepare_hilo", "proj_run_hilo", "proj_get_plan_hilo", "proj_num_candidates_hilo",
            "proj_candidate_name_hilo", "proj_run_candidate_hilo", "proj_packed_bytes", "proj_pack_weights",
            "proj_run_packed", "proj_get_plan_packed", "proj_num_candidates_packed", "proj_candidate_name_packed",
-           "proj_run_candidate_packed"]
+           "proj_run_candidate_packed", "proj_read_probe"]
 
 
 class ProjError(RuntimeError):
@@ -96,6 +97,7 @@ def lib() -> ctypes.CDLL:
         "proj_num_candidates_packed": ([i64, i64, i64, ci, ci, ci, ci], ci),
         "proj_candidate_name_packed": ([i64, i64, i64, ci, ci, ci, ci, ci, ctypes.c_char_p, ctypes.c_size_t], st),
         "proj_run_candidate_packed": ([vp, ci, vp, vp, ci, vp, ci, i64, i64, i64, vp, ci, vp], st),
+        "proj_read_probe": ([vp, vp, ctypes.c_size_t, vp], st),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -381,6 +383,14 @@ def proj_graph_capture(ctx, Xs, Ws, biases, Ys, epilogue, out_dtype=None, stream
     _check(lib().proj_graph_capture(ctx, n, xs, ws, bs, ys, int(epilogue), M, N, K,
                                     _out_dtype(Ys[0], out_dtype), _stream(stream), ctypes.byref(g)), ctx)
     return g.value
+
+
+def proj_read_probe(ctx, buf, stream=None) -> None:
+    """Enqueue one plain streaming read of the whole of tensor `buf` (its
+    bytes a multiple of 16): the measured read floor to time beside
+    proj_run on the same buffers."""
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().proj_read_probe(ctx, _ptr(buf), nbytes, _stream(stream)), ctx)
 
 
 def proj_graph_launch(graph, stream=None) -> None:

@@ -71,7 +71,40 @@ __global__ __launch_bounds__(256) void flush_read_kernel(const u32x4 *p, int64_t
     if (x == 0x9e3779b9u) sink[threadIdx.x] = x;
 }
 
+// A plain streaming read, the ceiling the weight-streaming kernels are
+// compared against: block b reads one contiguous slab of the buffer with
+// 16-byte non-temporal loads, eight in flight per thread.  Like the flush
+// read, the loads feed a store that happens only for one fixed value.
+__global__ __launch_bounds__(256) void read_probe_kernel(const u32x4 *p, int64_t n16, unsigned *sink) {
+    const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+    const int64_t b0 = static_cast<int64_t>(blockIdx.x) * per;
+    const int64_t b1 = b0 + per < n16 ? b0 + per : n16;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    int64_t i = b0 + threadIdx.x;
+    for (; i + 7 * 256 < b1; i += 8 * 256) {
+        u32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(p + i + u * 256);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc ^= v[u];
+    }
+    for (; i < b1; i += 256) acc ^= __builtin_nontemporal_load(p + i);
+    const unsigned x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+    if (x == 0x9e3779b9u) sink[threadIdx.x] = x;
+}
+
 #ifndef __HIP_DEVICE_COMPILE__
+hipError_t launch_read_probe(const void *buf, size_t bytes, unsigned *sink, hipStream_t st) {
+    const int64_t n16 = static_cast<int64_t>(bytes / 16);
+    if (n16 <= 0) return hipSuccess;
+    // 4096 slabs (16 per CU) of at least 32 KiB each
+    int64_t blocks = n16 / 2048;
+    blocks = blocks < 1 ? 1 : blocks > 4096 ? 4096 : blocks;
+    hipLaunchKernelGGL(read_probe_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
+                       static_cast<const u32x4 *>(buf), n16, sink);
+    return hipGetLastError();
+}
+
 hipError_t launch_flush(const void *buf, size_t bytes, unsigned *sink, hipStream_t st) {
     hipLaunchKernelGGL(flush_read_kernel, dim3(2048), dim3(256), 0, st, static_cast<const u32x4 *>(buf),
                        static_cast<int64_t>(bytes / 16), sink);

@@ -58,4 +58,8 @@ hipError_t launch_hilo_split(const float *W, int64_t N, int64_t K, uint16_t *out
 // `sink` needs room for 256 unsigned.
 hipError_t launch_flush(const void *buf, size_t bytes, unsigned *sink, hipStream_t st);
 
+// Plain streaming read of the first bytes/16 16-byte chunks of `buf`
+// (generic.hip); `sink` needs room for 256 unsigned.
+hipError_t launch_read_probe(const void *buf, size_t bytes, unsigned *sink, hipStream_t st);
+
 }  // namespace proj

@@ -846,6 +846,23 @@ proj_status proj_run_candidate_packed(proj_ctx *ctx, int index, const void *X, c
     return PROJ_OK;
 }
 
+proj_status proj_read_probe(proj_ctx *ctx, const void *buf, size_t bytes, void *stream) {
+    if (!ctx) return PROJ_ERR_INVALID_ARG;
+    if (ctx->magic == kDead) return PROJ_ERR_DESTROYED;
+    if (ctx->magic != kMagic) return PROJ_ERR_INVALID_ARG;
+    if (bytes == 0) return PROJ_OK;
+    if (!buf || reinterpret_cast<uintptr_t>(buf) % 16 || bytes % 16) {
+        set_err(ctx, "read probe: buffer NULL, or buffer or size not a multiple of 16 bytes");
+        return PROJ_ERR_INVALID_ARG;
+    }
+    DeviceGuard g(ctx->device);
+    // the split-K workspace holds nothing between calls: it takes the
+    // (practically never made) store
+    hipError_t e = launch_read_probe(buf, bytes, reinterpret_cast<unsigned *>(ctx->ws), static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(ctx, "launch", e);
+    return PROJ_OK;
+}
+
 proj_status proj_graph_capture(proj_ctx *ctx, int n_calls, const void *const *X, const void *const *W,
                                const void *const *bias, void *const *Y, int epi, int64_t M, int64_t N, int64_t K,
                                int out, void *stream, proj_graph **graph) {

@@ -248,6 +248,17 @@ proj_status proj_run_candidate_hilo(proj_ctx *ctx, int index, const void *X, con
                                     const void *bias, int epilogue, int64_t M, int64_t N,
                                     int64_t K, void *Y, int out_dtype, void *stream);
 
+/* Measured read floor (worklog "How I made Muse's GPU projections 1.32x faster
+ * in the Open Kernel Challenge", section "A rough way to ask how much room was
+ * left": timed plain reads of a weight-sized buffer as the practical floor a
+ * weight-streaming projection is compared with).  Enqueues on `stream` one
+ * plain streaming read of the `bytes` bytes at device address `buf`
+ * (contiguous slabs per workgroup, 16-byte non-temporal loads), so a caller
+ * can time it next to proj_run on the same buffers.  Reads only; computes
+ * nothing the caller sees.  buf and bytes must be multiples of 16
+ * (PROJ_ERR_INVALID_ARG otherwise); bytes = 0 is a no-op. */
+proj_status proj_read_probe(proj_ctx *ctx, const void *buf, size_t bytes, void *stream);
+
 /* HIP-graph capture of repeated launches (hot-path row: capture/replay).
  * Records n_calls proj_run calls, call i using X[i], W[i], bias[i], Y[i]
  * (bias may be NULL, or bias[i] NULL, when the epilogue has none), all with

@@ -264,3 +264,22 @@ def test_destroyed_handles_are_reported():
     buf = ctypes.create_string_buffer(64)
     assert L.proj_get_plan(c, 2, 4, 32, 0, 0, 1, buf, 64) == dlp.PROJ_ERR_DESTROYED
     assert L.proj_last_error(c) == b""
+
+
+def test_read_probe_reads_only(ctx):
+    """The read floor probe: whole and ragged sizes (fewer chunks than one
+    slab, a partial last slab) run and leave the buffer as it was; a
+    misaligned buffer or size is rejected."""
+    import torch
+    buf = torch.arange(1 << 20, dtype=torch.float32, device="cuda")   # 4 MiB
+    ref = buf.clone()
+    L = dlp.lib()
+    dlp.proj_read_probe(ctx, buf)
+    for n in (16, 48, 4096 + 16, 3 * 2048 * 16 + 32, (1 << 22) - 16):
+        assert L.proj_read_probe(ctx, buf.data_ptr(), n, None) == dlp.PROJ_OK
+    assert L.proj_read_probe(ctx, buf.data_ptr(), 0, None) == dlp.PROJ_OK
+    assert L.proj_read_probe(ctx, buf.data_ptr() + 4, 64, None) == dlp.PROJ_ERR_INVALID_ARG
+    assert L.proj_read_probe(ctx, buf.data_ptr(), 20, None) == dlp.PROJ_ERR_INVALID_ARG
+    assert L.proj_read_probe(ctx, None, 64, None) == dlp.PROJ_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert torch.equal(buf, ref)
