@@ -283,3 +283,20 @@ def test_read_probe_reads_only(ctx):
     assert L.proj_read_probe(ctx, None, 64, None) == dlp.PROJ_ERR_INVALID_ARG
     torch.cuda.synchronize()
     assert torch.equal(buf, ref)
+
+
+def test_project_helper_allocates_and_matches(ctx):
+    """dlp.project (allocates Y): bias + GELU to bf16 by default, fp32 on
+    request, both within tolerance of the oracle; no bias means no bias."""
+    import torch
+    M, N, K = 16, 520, 1024
+    X, W, b = synth.make_inputs(M, N, K, True, 17)
+    Xd, Wd, bd = dev_bf16(X), dev_bf16(W), dev_bf16(b)
+    Y = dlp.project(ctx, Xd, Wd, bd, gelu=True)
+    assert Y.dtype == torch.bfloat16 and tuple(Y.shape) == (M, N)
+    r, _ = oracle.reference(X, W, b, oracle.EPI_BIAS_GELU, oracle.OUT_BF16)
+    assert compare.check(host_f64(Y), r)["ok"]
+    Y32 = dlp.project(ctx, Xd, Wd, out_dtype=dlp.OUT_F32)
+    assert Y32.dtype == torch.float32
+    r32, _ = oracle.reference(X, W, None, oracle.EPI_NONE, oracle.OUT_F32)
+    assert compare.check(host_f64(Y32), r32)["ok"]
