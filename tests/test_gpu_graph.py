@@ -96,3 +96,38 @@ def test_capture_without_plan_uses_default(ctx, monkeypatch):
     assert "default" in dlp.proj_get_plan(ctx, M, N, K, 1, 1)
     r, _ = oracle.reference(X, W, b, 1, 1)
     assert compare.check(host_f64(Y), r)["ok"]
+
+
+def test_tune_refused_under_capture_then_replaces_default(ctx):
+    """Inside a stream capture, proj_tune returns PROJ_ERR_NOT_TUNED and
+    enqueues nothing, while proj_run of a first-seen shape records the
+    untimed default plan; the graph replays correctly.  Outside capture,
+    proj_tune then replaces the default with a measured plan, and the
+    result is the same within tolerance."""
+    import torch
+    M, N, K = 16, 272, 1536
+    X, W, b = synth.make_inputs(M, N, K, True, 23)
+    Xd, Wd, bd = dev_bf16(X), dev_bf16(W), dev_bf16(b)
+    Y = out_tensor(M, N, oracle.OUT_F32)
+    L = dlp.lib()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        st = torch.cuda.current_stream().cuda_stream
+        assert L.proj_tune(ctx, Xd.data_ptr(), Wd.data_ptr(), bd.data_ptr(), dlp.EPI_BIAS, M, N, K,
+                           Y.data_ptr(), dlp.OUT_F32, st) == dlp.PROJ_ERR_NOT_TUNED
+        assert L.proj_run(ctx, Xd.data_ptr(), Wd.data_ptr(), bd.data_ptr(), dlp.EPI_BIAS, M, N, K,
+                          Y.data_ptr(), dlp.OUT_F32, st) == dlp.PROJ_OK
+    r, _ = oracle.reference(X, W, b, oracle.EPI_BIAS, oracle.OUT_F32)
+    for _ in range(3):
+        Y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert compare.check(host_f64(Y), r)["ok"]
+    del g
+    assert dlp.proj_get_plan(ctx, M, N, K, dlp.EPI_BIAS, dlp.OUT_F32).endswith("(default)")
+    Y.fill_(float("nan"))
+    dlp.proj_tune(ctx, Xd, Wd, bd, dlp.EPI_BIAS, Y)
+    torch.cuda.synchronize()
+    assert "tuned" in dlp.proj_get_plan(ctx, M, N, K, dlp.EPI_BIAS, dlp.OUT_F32)
+    assert compare.check(host_f64(Y), r)["ok"]
