@@ -332,3 +332,25 @@ def test_two_contexts_on_two_streams(ctx):
             assert np.array_equal(host_f64(Y), r)
     finally:
         dlp.proj_destroy(c2)
+
+
+@pytest.mark.parametrize("shape", [(8, 96, 512), (40, 96, 256), (300, 192, 128)],
+                         ids=lambda s: "M%d_N%d_K%d" % s)
+def test_nonfinite_inputs_propagate_every_candidate(ctx, shape):
+    """IEEE propagation through every kernel family: a NaN in a row of X
+    makes that row of Y all NaN, an infinity makes it all non-finite (inf
+    or NaN, by the signs met), with bias and GELU too; other rows stay
+    finite."""
+    M, N, K = shape
+    X, W, b = synth.make_inputs(M, N, K, True, 31)
+    X = X.copy()
+    X[3, K // 3] = 0x7FC0        # NaN
+    X[5, 7] = 0x7F80             # +inf
+    Xd, Wd, bd = dev_bf16(X), dev_bf16(W), dev_bf16(b)
+    others = [m for m in range(M) if m not in (3, 5)]
+    for epi in (oracle.EPI_NONE, oracle.EPI_BIAS_GELU):
+        for i, name in enumerate(candidate_names(M, N, K, epi, oracle.OUT_BF16)):
+            u = run_candidate(ctx, i, Xd, Wd, bd, epi, M, N, K, oracle.OUT_BF16)
+            assert np.isnan(u[3]).all(), name
+            assert (~np.isfinite(u[5])).all(), name
+            assert np.isfinite(u[others]).all(), name
