@@ -48,6 +48,11 @@ def test_null_handles_rejected_before_any_hip_call():
     assert L.proj_create(None, 0) == dlp.PROJ_ERR_INVALID_ARG
     assert L.proj_graph_launch(None, None) == dlp.PROJ_ERR_INVALID_ARG
     assert L.proj_graph_destroy(None) == dlp.PROJ_ERR_INVALID_ARG
+    assert L.proj_read_probe(None, None, 64, None) == dlp.PROJ_ERR_INVALID_ARG
+    assert L.proj_prepare_hilo(None, None, 1, 1, None, None) == dlp.PROJ_ERR_INVALID_ARG
+    assert L.proj_pack_weights(None, None, 16, 128, 2, None, None) == dlp.PROJ_ERR_INVALID_ARG
+    assert L.proj_graph_capture(None, 1, None, None, None, None, 0, 1, 1, 1, 0, None, None) == \
+        dlp.PROJ_ERR_INVALID_ARG
     assert L.proj_last_error(None) == b""
 
 
