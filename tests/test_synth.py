@@ -46,9 +46,12 @@ def test_sweep_shapes_follow_the_table():
         assert (fam[("qkv_gate", M)].N, fam[("qkv_gate", M)].K) == (2304, 8192)
         assert (fam[("output", M)].N, fam[("output", M)].K) == (8192, 1024)
         assert (fam[("pooler", M)].N, fam[("pooler", M)].K) == (4096, 8192)
-        assert fam[("unpooler", M)].K == 4096 and fam[("unpooler", M)].N == (1024 if M <= 32 else 8192)
+        # the worklog's thirty-shape timing table: 1 / 1,024 / 4,096 and
+        # 8 / 1,024 / 4,096; every other load 8,192 / 4,096
+        assert fam[("unpooler", M)].K == 4096 and fam[("unpooler", M)].N == (1024 if M in (1, 8) else 8192)
         r = fam[("router", M)]
         assert (r.N, r.K, r.fp32_weights) == (256, 8192, True)
+    assert [fam[("unpooler", M)].N for M in (1, 8, 16, 32, 128, 256)] == [1024, 1024, 8192, 8192, 8192, 8192]
     X, W = synth.sweep_inputs(fam[("router", 1)])
     assert X.dtype == np.uint16 and W.dtype == np.float32 and W.shape == (256, 8192)
     assert abs(W.std() * np.sqrt(8192) - 1.0) < 0.02
