@@ -70,7 +70,7 @@ def lib() -> ctypes.CDLL:
     vp, i64, ci, st = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int
     run_args = [vp, vp, vp, vp, ci, i64, i64, i64, vp, ci, vp]
     sig = {
-        "proj_create": ([ctypes.POINTER(vp), ci], st),
+        "proj_create": ([ctypes.POINTER(vp), ci, ctypes.c_size_t], st),
         "proj_run": (run_args, st),
         "proj_tune": (run_args, st),
         "proj_destroy": ([vp], st),
@@ -170,9 +170,14 @@ def _check_operands(X, W, bias, Y):
 
 # ------------------------------------------------------------------ the ABI
 
-def proj_create(device: int = 0) -> int:
+DEFAULT_WORKSPACE_BYTES = 64 << 20
+
+
+def proj_create(device: int = 0, max_workspace_bytes: int = DEFAULT_WORKSPACE_BYTES) -> int:
+    """Create a context on `device` whose split-K workspace is
+    max_workspace_bytes (plans whose fp32 partials need more are not used)."""
     h = ctypes.c_void_p()
-    _check(lib().proj_create(ctypes.byref(h), int(device)))
+    _check(lib().proj_create(ctypes.byref(h), int(device), int(max_workspace_bytes)))
     return h.value
 
 

@@ -34,8 +34,8 @@ namespace {
 
 constexpr uint32_t kMagic = 0x50524f4au;   // live context
 constexpr uint32_t kDead = 0xdeadbeefu;    // destroyed context
-constexpr size_t kWorkspaceBytes = 64ull << 20;
-constexpr size_t kZeroBytes = 256;
+constexpr size_t kZeroBytes = 256;   // zero page for masked loads
+constexpr size_t kSinkBytes = 1024;  // target of the read kernels' never-taken store
 constexpr size_t kFlushBytes = 512ull << 20;  // larger than the last-level cache
 
 // K is the depth of the product: for a hi/lo weight pair (hilo = 1) twice
@@ -71,18 +71,23 @@ struct Plan {
 struct proj_ctx {
     uint32_t magic;
     int device;
-    int cus;  // compute units of the device
-    float *ws;
-    uint16_t *zeros;
-    void *flush;
+    int cus;             // compute units of the device
+    double cu_flops;     // one CU's dense bf16 matrix rate (flop/s) at the device clock
+    float *ws;           // split-K partial workspace, ws_bytes long (caller-bounded)
+    size_t ws_bytes;
+    uint16_t *zeros;     // kZeroBytes of zeros, then kSinkBytes of sink (one allocation)
     std::map<Key, Plan> plans;
     std::mutex mu;
     std::string err;
 };
 
+// A captured graph keeps the context's workspace and zero page as kernel
+// arguments, so it remembers its context: once that is destroyed the graph
+// is not replayed.
 struct proj_graph {
     uint32_t magic;
     int device;
+    proj_ctx *ctx;
     hipGraph_t graph;
     hipGraphExec_t exec;
 };
@@ -155,8 +160,10 @@ std::string gemm_name(const GemmVariant &v, int S) {
 }
 
 // Every compiled variant that can run this shape correctly.  These are
-// validity rules (operand alignment, tile coverage of M, workspace size),
-// not performance guesses; the measurement picks among them.
+// validity rules only (operand alignment, tile coverage of M, 32-bit buffer
+// offsets, a split covering at least one stage); the measurement picks among
+// them.  Whether a split's fp32 partials fit a context's workspace is decided
+// per context (workspace_bytes, fits).
 std::vector<Candidate> candidates(const Key &k) {
     std::vector<Candidate> out;
     if (k.wpack) {
@@ -175,7 +182,6 @@ std::vector<Candidate> candidates(const Key &k) {
             const int64_t tiles = (k.N + 16 * v.nt - 1) / (16 * v.nt);
             for (int S : {1, 2, 4, 8, 16}) {
                 if (S > 1 && S > stages) continue;
-                if (S > 1 && static_cast<size_t>(S) * k.M * k.N * sizeof(float) > kWorkspaceBytes) continue;
                 if (mblocks * tiles * S > 0x7fffffff) continue;
                 out.push_back({KIND_STREAM, i, S, stream_name(v, S)});
             }
@@ -206,7 +212,6 @@ std::vector<Candidate> candidates(const Key &k) {
                 const int64_t tiles = (k.N + 16 * v.nt - 1) / (16 * v.nt);
                 for (int S : {1, 2, 4, 8, 16}) {
                     if (S > 1 && S > stages) continue;
-                    if (S > 1 && static_cast<size_t>(S) * k.M * k.N * sizeof(float) > kWorkspaceBytes) continue;
                     if (mblocks * tiles * S > 0x7fffffff) continue;
                     out.push_back({KIND_STREAM, i, S, stream_name(v, S)});
                 }
@@ -223,7 +228,6 @@ std::vector<Candidate> candidates(const Key &k) {
                 const int64_t tiles = (k.N + v.rows - 1) / v.rows;
                 for (int S : {1, 2, 4, 8}) {
                     if (S > 1 && S > k.K / 8) continue;
-                    if (S > 1 && static_cast<size_t>(S) * k.M * k.N * sizeof(float) > kWorkspaceBytes) continue;
                     if (tiles * S > 0x7fffffff) continue;
                     out.push_back({KIND_GEMV, i, S, gemv_name(v, S)});
                 }
@@ -236,13 +240,11 @@ std::vector<Candidate> candidates(const Key &k) {
             if (k.hilo && (std::strcmp(v.family, "gemmpp64p") != 0 || (k.K / 2) % 64 != 0 || k.K < 128)) continue;
             if (v.kmax > 0 && k.K > v.kmax) continue;
             out.push_back({KIND_GEMM, i, 1, gemm_name(v, 1)});
-            // K splits: at least two 64-wide k-ranges each, partials fit the
-            // workspace, and split only while the tiles alone leave CUs idle
+            // K splits: at least two 64-wide k-ranges each
             const int64_t tiles = ((k.M + v.bm - 1) / v.bm) * ((k.N + v.bn - 1) / v.bn);
             for (int S = 2; S <= v.max_splits; S *= 2) {
                 if (k.K / 64 < 2 * static_cast<int64_t>(S)) break;
-                if (static_cast<size_t>(S) * k.M * k.N * sizeof(float) > kWorkspaceBytes) break;
-                if (tiles * (S / 2) >= 256) break;
+                if (tiles * S > 0x7fffffff) break;
                 out.push_back({KIND_GEMM, i, S, gemm_name(v, S)});
             }
         }
@@ -251,9 +253,30 @@ std::vector<Candidate> candidates(const Key &k) {
     return out;
 }
 
-// The untimed plan used under stream capture or with PROJ_TUNE=0.
-Candidate default_candidate(const Key &k) {
-    std::vector<Candidate> c = candidates(k);
+// Bytes of fp32 partials a candidate writes to the split-K workspace.
+size_t workspace_bytes(const Candidate &c, const Key &k) {
+    if (c.splits <= 1) return 0;
+    return static_cast<size_t>(c.splits) * static_cast<size_t>(k.M) * static_cast<size_t>(k.N) * sizeof(float);
+}
+
+// Whether a candidate can run with `ws` bytes of split-K workspace.
+bool fits(const Candidate &c, const Key &k, size_t ws) { return workspace_bytes(c, k) <= ws; }
+
+// The candidates that can run with `ws` bytes of split-K workspace (the
+// any-shape kernel, which needs none, when nothing else does).
+std::vector<Candidate> candidates_within(const Key &k, size_t ws) {
+    std::vector<Candidate> all = candidates(k), out;
+    for (const Candidate &c : all)
+        if (fits(c, k, ws)) out.push_back(c);
+    if (out.empty()) out.push_back({KIND_GENERIC, 0, 1, "generic"});
+    return out;
+}
+
+// The untimed plan used under stream capture or with PROJ_TUNE=0, among the
+// candidates that fit `ws` bytes of workspace on a device of `cus` compute
+// units.
+Candidate default_candidate(const Key &k, size_t ws, int cus) {
+    std::vector<Candidate> c = candidates_within(k, ws);
     auto find = [&](const char *name) -> const Candidate * {
         for (const Candidate &x : c)
             if (x.name == name) return &x;
@@ -269,7 +292,7 @@ Candidate default_candidate(const Key &k) {
                 const StreamVariant &v = kStreamVariants[x.variant];
                 if (v.nt != 2 || v.kc != 128 || v.waves != 4) continue;
                 if (pass == 0 ? !v.wnt : (v.wnt || v.depth != 5)) continue;
-                if (((k.N + 31) / 32) * x.splits >= 256 || x.splits == 8) return x;
+                if (((k.N + 31) / 32) * x.splits >= cus || x.splits == 8) return x;
             }
     }
     if (const Candidate *g = find("gemmpp64_256x256x64_w4x2_g4")) return *g;
@@ -278,6 +301,12 @@ Candidate default_candidate(const Key &k) {
     for (const Candidate &x : c)
         if (x.kind == KIND_GEMM) return x;
     return c.front();
+}
+
+proj_status no_workspace(proj_ctx *c, const Candidate &cand, const Key &k) {
+    set_err(c, "%s needs %zu bytes of split-K workspace; the context holds %zu (proj_create's bound)",
+            cand.name.c_str(), workspace_bytes(cand, k), c->ws_bytes);
+    return PROJ_ERR_NO_MEMORY;
 }
 
 Args make_args(proj_ctx *c, const void *X, const void *W, const void *bias, int epi, int64_t M, int64_t N,
@@ -415,31 +444,39 @@ Extent candidate_extent(const Candidate &c, const Key &k) {
 }
 
 // A time no run of the candidate can beat: the multiply-adds its tiles
-// cover (2 Mp Np K) at one CU's share of the published dense bf16 matrix
-// peak (2.5 PFLOP/s over 256 CUs) on each CU it occupies.  The tuner does not
-// launch candidates whose bound is far above the best time already measured
-// (a 256-row GEMM tile walking a very long K for 16 token rows alone would
-// take milliseconds to seconds).
-double lower_bound_us(const Candidate &c, const Key &k, int cus) {
+// cover (2 Mp Np K) at one CU's dense bf16 matrix rate (cu_flops, from the
+// device clock) on each CU it occupies.  The tuner does not launch
+// candidates whose bound is far above the best time already measured (a
+// 256-row GEMM tile walking a very long K for 16 token rows alone would take
+// milliseconds to seconds).
+double lower_bound_us(const Candidate &c, const Key &k, int cus, double cu_flops) {
     const Extent e = candidate_extent(c, k);
     const double wgs = std::max<double>(1.0, std::min<double>(static_cast<double>(e.wgs), cus));
-    const double per_cu = 2.5e15 / 256.0;
-    return 2.0 * static_cast<double>(e.mp) * static_cast<double>(e.np) * static_cast<double>(k.K) / (wgs * per_cu) *
-           1e6;
+    return 2.0 * static_cast<double>(e.mp) * static_cast<double>(e.np) * static_cast<double>(k.K) /
+           (wgs * cu_flops) * 1e6;
 }
 constexpr double kSkipFactor = 20.0;
 
-// Time every candidate on the caller's buffers; returns the winner.  The
-// last-level cache is flushed before each timed run when the operands could
-// fit in it, so small shapes are timed as they run from HBM.
+// Time every candidate that fits the context's workspace on the caller's
+// buffers; returns the winner.  The last-level cache is flushed before each
+// timed run when the operands could fit in it, so small shapes are timed as
+// they run from HBM: the flush buffer (kFlushBytes) is allocated for the
+// tuning run and freed before returning.
 proj_status tune(proj_ctx *c, const Key &k, const Args &a, hipStream_t st, Plan &plan) {
-    std::vector<Candidate> cands = candidates(k);
+    std::vector<Candidate> cands = candidates_within(k, c->ws_bytes);
     const size_t bytes = static_cast<size_t>(2 * (k.M + k.N) * k.K);
-    const bool flush = bytes < kFlushBytes;
-    if (flush && !c->flush) {
-        if (hipMalloc(&c->flush, kFlushBytes + 1024) != hipSuccess) c->flush = nullptr;
+    void *fbuf = nullptr;
+    if (bytes < kFlushBytes && hipMalloc(&fbuf, kFlushBytes + 1024) != hipSuccess) {
+        (void)hipGetLastError();
+        fbuf = nullptr;  // tune without flushing
     }
-    unsigned *sink = c->flush ? reinterpret_cast<unsigned *>(static_cast<char *>(c->flush) + kFlushBytes) : nullptr;
+    struct FreeAfter {
+        void *p;
+        ~FreeAfter() {
+            if (p) hipFree(p);
+        }
+    } free_after{fbuf};
+    unsigned *sink = fbuf ? reinterpret_cast<unsigned *>(static_cast<char *>(fbuf) + kFlushBytes) : nullptr;
     hipEvent_t e0, e1;
     if (hipEventCreate(&e0) != hipSuccess) return hip_fail(c, "hipEventCreate", hipGetLastError());
     if (hipEventCreate(&e1) != hipSuccess) {
@@ -449,7 +486,7 @@ proj_status tune(proj_ctx *c, const Key &k, const Args &a, hipStream_t st, Plan 
     // one timed run of candidate i (after a cache flush where that applies);
     // a negative time if it could not run
     auto time_once = [&](size_t i) -> float {
-        if (flush && c->flush) launch_flush(c->flush, kFlushBytes, sink, st);
+        if (fbuf) launch_flush(fbuf, kFlushBytes, sink, st);
         hipEventRecord(e0, st);
         if (launch(cands[i], a, st) != hipSuccess) return -1.f;
         hipEventRecord(e1, st);
@@ -466,7 +503,8 @@ proj_status tune(proj_ctx *c, const Key &k, const Args &a, hipStream_t st, Plan 
     std::vector<std::pair<float, size_t>> ranked;
     float best_so_far = -1.f;
     for (size_t i = 0; i < cands.size(); ++i) {
-        if (best_so_far > 0.f && lower_bound_us(cands[i], k, c->cus) > kSkipFactor * best_so_far) continue;
+        if (best_so_far > 0.f && lower_bound_us(cands[i], k, c->cus, c->cu_flops) > kSkipFactor * best_so_far)
+            continue;
         if (launch(cands[i], a, st) != hipSuccess) {  // warm-up; skip variants that cannot launch
             (void)hipGetLastError();
             continue;
@@ -516,9 +554,12 @@ proj_status tune(proj_ctx *c, const Key &k, const Args &a, hipStream_t st, Plan 
         }
     }
     plan = Plan{cands[best_i], true, best};
-    // leave the winner's result in Y
+    // leave the winner's result in Y (and let the flush buffer go only once
+    // the timed runs that read it are done)
     hipError_t e = launch(plan.cand, a, st);
     if (e != hipSuccess) return hip_fail(c, "launch", e);
+    e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(c, "hipStreamSynchronize", e);
     return PROJ_OK;
 }
 
@@ -550,7 +591,7 @@ proj_status run_impl(proj_ctx *c, const void *X, const void *W, const void *bias
             c->plans[k] = p;
             return PROJ_OK;  // tune() already left the winner's result in Y
         }
-        p = Plan{default_candidate(k), false, 0.f};
+        p = Plan{default_candidate(k, c->ws_bytes, c->cus), false, 0.f};
         it = c->plans.insert_or_assign(k, p).first;
     } else if (force_tune) {
         // already tuned: just run it
@@ -564,7 +605,7 @@ proj_status run_impl(proj_ctx *c, const void *X, const void *W, const void *bias
 
 extern "C" {
 
-proj_status proj_create(proj_ctx **out, int device) {
+proj_status proj_create(proj_ctx **out, int device, size_t max_workspace_bytes) {
     if (!out) return PROJ_ERR_INVALID_ARG;
     *out = nullptr;
     int n = 0;
@@ -578,13 +619,25 @@ proj_status proj_create(proj_ctx **out, int device) {
     if (!c) return PROJ_ERR_NO_MEMORY;
     c->magic = kMagic;
     c->device = device;
-    c->cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
+    c->cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1;
+    // each CU's 4 SIMDs issue one 16x16x32 bf16 matrix op (16,384 flops)
+    // every 16 cycles; clockRate is in kHz
+    c->cu_flops = 4.0 * 16384.0 / 16.0 * (prop.clockRate > 0 ? prop.clockRate : 1) * 1e3;
     c->ws = nullptr;
+    c->ws_bytes = 0;
     c->zeros = nullptr;
-    c->flush = nullptr;
-    bool ok = hipMalloc(&c->ws, kWorkspaceBytes) == hipSuccess &&
-              hipMalloc(&c->zeros, kZeroBytes) == hipSuccess &&
-              hipMemset(c->zeros, 0, kZeroBytes) == hipSuccess;
+    bool ok = hipMalloc(&c->zeros, kZeroBytes + kSinkBytes) == hipSuccess &&
+              hipMemset(c->zeros, 0, kZeroBytes + kSinkBytes) == hipSuccess;
+    if (ok && max_workspace_bytes > 0) {
+        const size_t ws = max_workspace_bytes / 256 * 256;
+        if (ws > 0 && hipMalloc(&c->ws, ws) != hipSuccess) {
+            (void)hipGetLastError();
+            hipFree(c->zeros);
+            delete c;
+            return PROJ_ERR_NO_MEMORY;
+        }
+        c->ws_bytes = ws;
+    }
     for (int i = 0; ok && i < kNumGemmVariants; ++i) ok = kGemmVariants[i].prepare() == hipSuccess;
     for (int i = 0; ok && i < kNumStreamVariants; ++i) ok = kStreamVariants[i].prepare() == hipSuccess;
     ok = ok && hipDeviceSynchronize() == hipSuccess;
@@ -687,14 +740,14 @@ proj_status proj_destroy(proj_ctx *ctx) {
         hipDeviceSynchronize();
         hipFree(ctx->ws);
         hipFree(ctx->zeros);
-        if (ctx->flush) hipFree(ctx->flush);
     }
     // the struct itself stays allocated as a marker, so a later use or a
-    // second destroy of this handle reads valid memory and is reported
+    // second destroy of this handle (or a replay of one of its graphs) reads
+    // valid memory and is reported
     std::lock_guard<std::mutex> lock(ctx->mu);
     ctx->ws = nullptr;
+    ctx->ws_bytes = 0;
     ctx->zeros = nullptr;
-    ctx->flush = nullptr;
     std::map<Key, Plan>().swap(ctx->plans);
     ctx->magic = kDead;
     return PROJ_OK;
@@ -774,6 +827,7 @@ proj_status proj_run_candidate_hilo(proj_ctx *ctx, int index, const void *X, con
         set_err(ctx, "candidate %d out of range (%d)", index, static_cast<int>(c.size()));
         return PROJ_ERR_INVALID_ARG;
     }
+    if (!fits(c[index], k, ctx->ws_bytes)) return no_workspace(ctx, c[index], k);
     DeviceGuard g(ctx->device);
     hipError_t e = launch(c[index], make_args(ctx, X, Whl, bias, epi, M, N, 2 * K, Y, out, 1),
                           static_cast<hipStream_t>(stream));
@@ -801,6 +855,7 @@ proj_status proj_run_candidate(proj_ctx *ctx, int index, const void *X, const vo
         set_err(ctx, "candidate %d out of range (%d)", index, static_cast<int>(c.size()));
         return PROJ_ERR_INVALID_ARG;
     }
+    if (!fits(c[index], k, ctx->ws_bytes)) return no_workspace(ctx, c[index], k);
     DeviceGuard g(ctx->device);
     hipError_t e = launch(c[index], make_args(ctx, X, W, bias, epi, M, N, K, Y, out), static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(ctx, "launch", e);
@@ -839,6 +894,7 @@ proj_status proj_run_candidate_packed(proj_ctx *ctx, int index, const void *X, c
         set_err(ctx, "candidate %d out of range (%d)", index, static_cast<int>(c.size()));
         return PROJ_ERR_INVALID_ARG;
     }
+    if (!fits(c[index], k, ctx->ws_bytes)) return no_workspace(ctx, c[index], k);
     DeviceGuard g(ctx->device);
     hipError_t e = launch(c[index], make_args(ctx, X, Wp, bias, epi, M, N, K, Y, out, 0, tile16),
                           static_cast<hipStream_t>(stream));
@@ -856,9 +912,8 @@ proj_status proj_read_probe(proj_ctx *ctx, const void *buf, size_t bytes, void *
         return PROJ_ERR_INVALID_ARG;
     }
     DeviceGuard g(ctx->device);
-    // the split-K workspace holds nothing between calls: it takes the
-    // (practically never made) store
-    hipError_t e = launch_read_probe(buf, bytes, reinterpret_cast<unsigned *>(ctx->ws), static_cast<hipStream_t>(stream));
+    unsigned *sink = reinterpret_cast<unsigned *>(reinterpret_cast<char *>(ctx->zeros) + kZeroBytes);
+    hipError_t e = launch_read_probe(buf, bytes, sink, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(ctx, "launch", e);
     return PROJ_OK;
 }
@@ -903,7 +958,7 @@ proj_status proj_graph_capture(proj_ctx *ctx, int n_calls, const void *const *X,
         hipGraphDestroy(gr);
         return hip_fail(ctx, "hipGraphInstantiate", e);
     }
-    proj_graph *pg = new (std::nothrow) proj_graph{kMagic, ctx->device, gr, ex};
+    proj_graph *pg = new (std::nothrow) proj_graph{kMagic, ctx->device, ctx, gr, ex};
     if (!pg) {
         hipGraphExecDestroy(ex);
         hipGraphDestroy(gr);
@@ -917,6 +972,9 @@ proj_status proj_graph_launch(proj_graph *g, void *stream) {
     if (!g) return PROJ_ERR_INVALID_ARG;
     if (g->magic == kDead) return PROJ_ERR_DESTROYED;
     if (g->magic != kMagic) return PROJ_ERR_INVALID_ARG;
+    // the graph's kernels take the context's workspace and zero page: a
+    // destroyed context's memory is gone (its struct stays as a marker)
+    if (g->ctx->magic != kMagic) return PROJ_ERR_DESTROYED;
     DeviceGuard dg(g->device);
     if (hipGraphLaunch(g->exec, static_cast<hipStream_t>(stream)) != hipSuccess) return PROJ_ERR_HIP;
     return PROJ_OK;

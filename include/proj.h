@@ -32,11 +32,16 @@
  *
  * Streams: `stream` is a hipStream_t passed as void* (NULL = the legacy
  * default stream).  Once a shape's plan is chosen (the first uncaptured call
- * for a shape measures the candidate plans, synchronising the stream and
- * possibly allocating a 512 MiB buffer used to flush caches while timing;
- * see proj_run), proj_run only enqueues work and returns: it never
+ * for a shape measures the candidate plans, synchronising the stream; while
+ * it times small shapes it holds a 512 MiB buffer that it reads to flush the
+ * caches, allocated for that tuning call and freed before it returns; see
+ * proj_run), proj_run only enqueues work and returns: it never
  * synchronises, allocates or reads device memory on the host, so it may be
  * recorded into a HIP graph (stream capture) -- see "Capture" below.
+ *
+ * Memory the library owns: per context, the split-K workspace (exactly the
+ * caller's bound, given to proj_create) and 1.25 KiB of zero page and sink;
+ * per tuning call, the flush buffer above.  Nothing else.
  *
  * Errors: every call returns a proj_status; nothing throws across the ABI.
  * Arguments are validated before any HIP call.  HIP failures return
@@ -82,11 +87,26 @@ typedef enum {
     PROJ_OUT_BF16 = 1  /* bf16 output, round to nearest even from fp32 */
 } proj_out_dtype;
 
-/* Create a context on HIP device `device`.  Allocates the split-K partial
- * workspace (64 MiB) and a zero page used for masked loads.
- * Returns PROJ_ERR_INVALID_ARG if ctx is NULL, PROJ_ERR_HIP if the device
- * cannot be used (e.g. no GPU), PROJ_ERR_UNSUPPORTED if it is not gfx950. */
-proj_status proj_create(proj_ctx **ctx, int device);
+/* Create a context on HIP device `device`.
+ *
+ * max_workspace_bytes bounds the split-K partial workspace: plans that split
+ * K over S workgroups write S fp32 partials of [M][N] (S * M * N * 4 bytes)
+ * there before a second kernel sums them (worklog "How I made Muse's GPU
+ * projections 1.32x faster in the Open Kernel Challenge", section "The
+ * temporary array is a real cost").  The workspace is allocated here, at
+ * that size rounded down to 256 bytes; 0 allocates none, and every plan then
+ * keeps K whole.  The planner only chooses plans whose partials fit, tuned or
+ * default, so proj_run never needs more; proj_run_candidate (and its _hilo /
+ * _packed forms) returns PROJ_ERR_NO_MEMORY for a candidate whose partials
+ * do not fit, also while the stream captures.  64 MiB covers every split of
+ * the weight-streaming shapes up to 64 token rows x 65,536 outputs at S = 4.
+ * A 256-byte zero page (masked loads) and a 1 KiB sink are also allocated.
+ *
+ * Returns PROJ_ERR_INVALID_ARG if ctx is NULL or the device index is out of
+ * range, PROJ_ERR_HIP if the device cannot be used (e.g. no GPU),
+ * PROJ_ERR_UNSUPPORTED if it is not gfx950, PROJ_ERR_NO_MEMORY if the
+ * workspace cannot be allocated. */
+proj_status proj_create(proj_ctx **ctx, int device, size_t max_workspace_bytes);
 
 /* Enqueue Y = epilogue(X . W^T [+ bias]) on `stream`.
  *
@@ -100,7 +120,8 @@ proj_status proj_create(proj_ctx **ctx, int device);
  * weight-streaming kernel with MFMA (M <= 64, and up to 512 in row blocks),
  * MFMA GEMMs (any M, K a multiple of 32 or 64), and an any-shape kernel;
  * K may be split over workgroups, with a second kernel adding the fp32
- * partials in split order and applying the epilogue.
+ * partials in split order and applying the epilogue (only plans whose
+ * partials fit the context's workspace are considered).
  *
  * Plan choice (kernel family, tile shape, split count): on the first call
  * for a shape key (M, N, K, epilogue, out dtype, alignment) outside stream
@@ -229,8 +250,8 @@ proj_status proj_candidate_name(int64_t M, int64_t N, int64_t K, int epilogue,
 
 /* Enqueue one specific candidate (index as above), bypassing the plan
  * cache.  Same argument rules as proj_run; PROJ_ERR_INVALID_ARG for an
- * index out of range, PROJ_ERR_NO_MEMORY if its split workspace does not
- * fit the context's. */
+ * index out of range, PROJ_ERR_NO_MEMORY (nothing enqueued) if its split-K
+ * partials need more than the context's workspace (proj_create's bound). */
 proj_status proj_run_candidate(proj_ctx *ctx, int index, const void *X, const void *W,
                                const void *bias, int epilogue, int64_t M, int64_t N,
                                int64_t K, void *Y, int out_dtype, void *stream);
@@ -272,12 +293,16 @@ proj_status proj_graph_capture(proj_ctx *ctx, int n_calls, const void *const *X,
                                int64_t K, int out_dtype, void *stream,
                                proj_graph **graph);
 
-/* Enqueue one replay of the graph on `stream`. */
+/* Enqueue one replay of the graph on `stream`.  The graph's kernels use its
+ * context's workspace: once that context is destroyed, the graph is not
+ * replayed and PROJ_ERR_DESTROYED is returned (nothing enqueued).  Destroy a
+ * context's graphs before the context; proj_destroy waits for replays
+ * already enqueued. */
 proj_status proj_graph_launch(proj_graph *graph, void *stream);
 
 /* Free the graph (does not synchronise; the caller waits for replays).  As
  * with contexts, the handle stays allocated as a marker and later calls with
- * it return PROJ_ERR_DESTROYED. */
+ * it return PROJ_ERR_DESTROYED.  Allowed after its context is destroyed. */
 proj_status proj_graph_destroy(proj_graph *graph);
 
 #ifdef __cplusplus

@@ -45,7 +45,7 @@ def test_null_handles_rejected_before_any_hip_call():
     assert L.proj_run(None, None, None, None, 0, 1, 1, 1, None, 0, None) == dlp.PROJ_ERR_INVALID_ARG
     assert L.proj_tune(None, None, None, None, 0, 1, 1, 1, None, 0, None) == dlp.PROJ_ERR_INVALID_ARG
     assert L.proj_destroy(None) == dlp.PROJ_ERR_INVALID_ARG
-    assert L.proj_create(None, 0) == dlp.PROJ_ERR_INVALID_ARG
+    assert L.proj_create(None, 0, 0) == dlp.PROJ_ERR_INVALID_ARG
     assert L.proj_graph_launch(None, None) == dlp.PROJ_ERR_INVALID_ARG
     assert L.proj_graph_destroy(None) == dlp.PROJ_ERR_INVALID_ARG
     assert L.proj_read_probe(None, None, 64, None) == dlp.PROJ_ERR_INVALID_ARG
@@ -122,3 +122,22 @@ def test_offset_limits_in_candidate_lists():
     assert gemv and not any("_r16_" in x for x in gemv)
     n = dlp.proj_num_candidates(1, 1024, 1 << 20, 0, 0)
     assert any("_r16_" in dlp.proj_candidate_name(1, 1024, 1 << 20, 0, 0, i) for i in range(n))
+
+
+def test_candidate_lists_hold_validity_rules_only():
+    """The candidate list carries no device or workspace threshold: every K
+    split that leaves each split at least two 64-wide k-ranges is listed for
+    the persistent GEMM, however many tiles the shape has, and streaming
+    splits are listed even where their fp32 partials exceed any default
+    workspace (a context keeps only those that fit its own bound)."""
+    def names(M, N, K, epi=0, out=1):
+        return [dlp.proj_candidate_name(M, N, K, epi, out, i)
+                for i in range(dlp.proj_num_candidates(M, N, K, epi, out))]
+    qkv = names(8192, 3072, 1024, 1, 1)                  # 512 tiles of 256 x 192, K / 64 = 16
+    for S in (2, 4, 8):
+        assert "gemmpp64p_256x192x64_w4x2_g4_s%d" % S in qkv
+    assert "gemmpp64p_256x192x64_w4x2_g4_s16" not in qkv    # a split would hold one k-range
+    ffn = names(4096, 8192, 8192, 3, 1)                  # 512 tiles of 256 x 256, K / 64 = 128
+    assert "gemmpp64p_256x256x64_w4x2_g4_s16" in ffn
+    wide = names(64, 131072, 8192)                       # S = 16 partials: 512 MiB
+    assert any(x.startswith("stream_mt4_") and x.endswith("_s16") for x in wide)

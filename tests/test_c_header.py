@@ -26,7 +26,7 @@ int main(void) {
     if (proj_packed_bytes(100, 200, 1) != -1) return 5;
     if (proj_run(NULL, NULL, NULL, NULL, 0, 1, 1, 1, NULL, 0, NULL) != PROJ_ERR_INVALID_ARG) return 6;
     proj_ctx *ctx = NULL;
-    proj_status s = proj_create(&ctx, 0);
+    proj_status s = proj_create(&ctx, 0, (size_t)64 << 20);
     if (s == PROJ_OK) proj_destroy(ctx);
     printf("%s|%s\n", name, proj_status_string(s));
     return 0;
