@@ -18,7 +18,10 @@ graph nodes, so it is an upper bound on the kernel's own duration).
 Prints ONE JSON line.  Default workload: M=16 K=8192 N=8192, bias, bf16 out.
 Beside the row-major figure the line carries the same steps with W
 registered in the packed tile layout (`packed_weights`), five repeat trials,
-a cache-resident (warm) figure, the oracle's CPU rate and the device.
+a cache-resident (warm) figure, the oracle's CPU rate and the device, and
+under `workloads` the other four workloads, each set up and timed the same
+way in the same process (time per call, roofline against its own bound,
+plan; --no-workloads skips them).
 
 Other modes: --sweep (the thirty-shape set, torch timed alongside),
 --candidate NAME (one plan repeated, for counter passes), --copy-calibration
@@ -531,6 +534,137 @@ def run_candidate(args) -> int:
     return 0
 
 
+class WorkloadRun:
+    """One workload set up for timing: P rotating buffer sets (distinct
+    allocations of X, W, bias, Y; together more than twice the last-level
+    cache), the plan tuned on the first call of each set, and HIP graphs
+    holding R calls that cycle over the sets (plus a tail graph so that
+    exactly `steps` calls are replayed)."""
+
+    def __init__(self, ctx, w, inputs, args, dev, stream):
+        import numpy as np
+        import torch
+
+        import dense_linear_projection_amd as dlp
+        import synth
+
+        X, W, b = inputs
+        self.ctx, self.w, self.stream, self.args = ctx, w, stream, args
+        set_bytes = w.alg_bytes()
+        P = max(1, -(-(2 * LLC_BYTES) // set_bytes))      # working set > 2x the LLC
+        self.P = P = min(P, 16)
+        to_dev = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        W0 = to_dev(W)
+        self.b0 = b0 = to_dev(b) if b is not None else None
+        self.Xs, self.Ws, self.bs, self.Ys = [], [], [], []
+        out_t = torch.float32 if w.out_dtype == synth.OUT_F32 else torch.bfloat16
+        for p in range(P):
+            self.Xs.append(to_dev(synth.normal_bf16((w.M, w.K), 1.0, 1000 + w.index + 100 * p)))
+            self.Ws.append(W0 if p == 0 else W0.clone())
+            self.bs.append(None if b0 is None else (b0 if p == 0 else b0.clone()))
+            self.Ys.append(torch.empty((w.M, w.N), dtype=out_t, device=dev))
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            for p in range(P):                       # plan tuning happens on the first call
+                dlp.proj_run(ctx, self.Xs[p], self.Ws[p], self.bs[p], w.epi, self.Ys[p], stream=stream)
+        stream.synchronize()
+        self.plan = dlp.proj_get_plan(ctx, w.M, w.N, w.K, w.epi, w.out_dtype)
+        # one graph holds R calls cycling over the P buffer sets
+        self.R = R = args.graph_calls or max(P, min(args.steps, 200) // P * P)
+        self.idx = idx = [i % P for i in range(R)]
+        self.g = self._capture(idx)
+        tail = args.steps % R
+        self.g_tail = self._capture([i % P for i in range(tail)]) if tail else None
+        # warmup (untimed)
+        for _ in range(max(1, args.warmup // R)):
+            dlp.proj_graph_launch(self.g, stream=stream)
+        stream.synchronize()
+        torch.cuda.synchronize()
+
+    def _capture(self, idx):
+        import dense_linear_projection_amd as dlp
+        return dlp.proj_graph_capture(self.ctx, [self.Xs[i] for i in idx], [self.Ws[i] for i in idx],
+                                      [self.bs[i] for i in idx] if self.b0 is not None else None,
+                                      [self.Ys[i] for i in idx], self.w.epi, stream=self.stream)
+
+    def time_steps(self, steps, e0, e1) -> float:
+        """Exactly `steps` calls from the graphs between HIP events recorded
+        on the launch stream, with device synchronisation on both sides;
+        returns milliseconds per call."""
+        import torch
+
+        import dense_linear_projection_amd as dlp
+        torch.cuda.synchronize()
+        e0.record(self.stream)
+        for _ in range(steps // self.R):
+            dlp.proj_graph_launch(self.g, stream=self.stream)
+        if self.g_tail is not None:
+            dlp.proj_graph_launch(self.g_tail, stream=self.stream)
+        e1.record(self.stream)
+        e1.synchronize()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    def close(self):
+        import dense_linear_projection_amd as dlp
+        dlp.proj_graph_destroy(self.g)
+        if self.g_tail is not None:
+            dlp.proj_graph_destroy(self.g_tail)
+        self.Xs = self.Ws = self.bs = self.Ys = self.b0 = None
+
+
+def roofline(w, plan, ms_per_step) -> dict:
+    """The roofline object of the bench line for workload w: algorithmic
+    bytes (weight-streaming workloads, M <= 64) or flops (GEMMs) per call
+    over the time per call, against the published HBM or bf16 matrix peak;
+    `traffic` from committed counter runs of the same kernel, if any."""
+    sec = ms_per_step / 1e3
+    gbs = w.alg_bytes() / sec / 1e9
+    tflops = w.alg_flops() / sec / 1e12
+    traffic = load_traffic(w.name, plan.split(" ")[0])
+    if w.M <= 64:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": traffic}
+    roof["kernel"] = plan.split(" ")[0]
+    roof["avg_kernel_us"] = round(ms_per_step * 1e3, 3)
+    roof["alg_bytes_per_launch"] = w.alg_bytes()
+    roof["alg_flops_per_launch"] = w.alg_flops()
+    return roof
+
+
+def time_other_workloads(ctx, headline, args, dev, stream) -> dict:
+    """The other four workloads, each set up and timed as the headline is
+    (same rotation rule, graph replay and step count, same process and
+    context): per workload the time per call, its roofline against its own
+    bound, and the plan."""
+    import torch
+
+    import synth
+    out = {}
+    for w in synth.WORKLOADS:
+        if w.index == headline.index:
+            continue
+        print("timing workload %s" % w.name, file=sys.stderr, flush=True)
+        run = WorkloadRun(ctx, w, synth.workload_inputs(w), args, dev, stream)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        ms = run.time_steps(args.steps, e0, e1)
+        out[w.name] = {"M": w.M, "N": w.N, "K": w.K, "epilogue": w.epi,
+                       "out_dtype": "fp32" if w.out_dtype == synth.OUT_F32 else "bf16",
+                       "ms_per_step": round(ms, 6), "plan": run.plan, "rotating_sets": run.P,
+                       "graph_calls": run.R, "gbs": round(w.alg_bytes() / (ms / 1e3) / 1e9, 1),
+                       "tflops": round(w.alg_flops() / (ms / 1e3) / 1e12, 2),
+                       "roofline": roofline(w, run.plan, ms)}
+        run.close()
+        del run
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -555,6 +689,8 @@ def main() -> int:
                     help="run the first candidate plan whose name contains this text --reps times on the "
                          "workload (for hardware counters; prints only its name and mean time)")
     ap.add_argument("--reps", type=int, default=12, help="runs for --candidate")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="time only the headline workload (skip the other four)")
     ap.add_argument("--plans", nargs="+", default=[],
                     help="for --ingest: one-pass stream plans to take counters for")
     args = ap.parse_args()
@@ -586,77 +722,21 @@ def main() -> int:
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     ctx = dlp.proj_create(0)
+    stream = torch.cuda.Stream()
 
     X, W, b = synth.workload_inputs(w)
-    set_bytes = w.alg_bytes()
-    P = max(1, -(-(2 * LLC_BYTES) // set_bytes))      # working set > 2x the LLC
-    P = min(P, 16)
-    to_dev = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
-    W0 = to_dev(W)
-    b0 = to_dev(b) if b is not None else None
-    Xs, Ws, bs, Ys = [], [], [], []
-    out_t = torch.float32 if w.out_dtype == synth.OUT_F32 else torch.bfloat16
-    for p in range(P):
-        Xs.append(to_dev(synth.normal_bf16((w.M, w.K), 1.0, 1000 + w.index + 100 * p)))
-        Ws.append(W0 if p == 0 else W0.clone())
-        bs.append(None if b0 is None else (b0 if p == 0 else b0.clone()))
-        Ys.append(torch.empty((w.M, w.N), dtype=out_t, device=dev))
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.Stream()
-    with torch.cuda.stream(stream):
-        for p in range(P):                       # plan tuning happens on the first call
-            dlp.proj_run(ctx, Xs[p], Ws[p], bs[p], w.epi, Ys[p], stream=stream)
-    stream.synchronize()
-    plan = dlp.proj_get_plan(ctx, w.M, w.N, w.K, w.epi, w.out_dtype)
-
-    # one graph holds R calls cycling over the P buffer sets
-    R = args.graph_calls or max(P, min(args.steps, 200) // P * P)
-    idx = [i % P for i in range(R)]
-    g = dlp.proj_graph_capture(ctx, [Xs[i] for i in idx], [Ws[i] for i in idx],
-                               [bs[i] for i in idx] if b0 is not None else None,
-                               [Ys[i] for i in idx], w.epi, stream=stream)
-    tail = args.steps % R
-    g_tail = None
-    if tail:
-        g_tail = dlp.proj_graph_capture(ctx, [Xs[i % P] for i in range(tail)], [Ws[i % P] for i in range(tail)],
-                                        [bs[i % P] for i in range(tail)] if b0 is not None else None,
-                                        [Ys[i % P] for i in range(tail)], w.epi, stream=stream)
-
-    # warmup (untimed)
-    for _ in range(max(1, args.warmup // R)):
-        dlp.proj_graph_launch(g, stream=stream)
-    stream.synchronize()
-    torch.cuda.synchronize()
-
+    run = WorkloadRun(ctx, w, (X, W, b), args, dev, stream)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps // R):
-        dlp.proj_graph_launch(g, stream=stream)
-    if g_tail is not None:
-        dlp.proj_graph_launch(g_tail, stream=stream)
-    e1.record(stream)
-    e1.synchronize()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1)
-    ms_per_step = ms / args.steps
+    ms_per_step = run.time_steps(args.steps, e0, e1)   # the contract's timed region
+    P, R, plan, idx = run.P, run.R, run.plan, run.idx
+    Xs, Ws, bs, Ys, g, g_tail, b0 = run.Xs, run.Ws, run.bs, run.Ys, run.g, run.g_tail, run.b0
     sec = ms_per_step / 1e3
 
     gbs = w.alg_bytes() / sec / 1e9
     tflops = w.alg_flops() / sec / 1e12
     hbm_bound = w.M <= 64
-    traffic = load_traffic(w.name, plan.split(" ")[0])
-    if hbm_bound:
-        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
-    else:
-        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": traffic}
-    roof["kernel"] = plan.split(" ")[0]
-    roof["avg_kernel_us"] = round(ms_per_step * 1e3, 3)
-    roof["alg_bytes_per_launch"] = w.alg_bytes()
-    roof["alg_flops_per_launch"] = w.alg_flops()
+    roof = roofline(w, plan, ms_per_step)
 
     # Outside the contract's timed region: the same K steps repeated TRIALS
     # times (median, min, max per step), and a warm number with one buffer
@@ -701,9 +781,11 @@ def main() -> int:
     if args.packed > 0:
         packed = time_packed(ctx, w, args, Xs, Ws, bs, Ys, idx, stream)
 
-    dlp.proj_graph_destroy(g)
-    if g_tail is not None:
-        dlp.proj_graph_destroy(g_tail)
+    run.close()
+    del Xs, Ws, bs, Ys, g, g_tail, b0
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    others = None if args.no_workloads else time_other_workloads(ctx, w, args, dev, stream)
     dlp.proj_destroy(ctx)
 
     line = {
@@ -732,6 +814,8 @@ def main() -> int:
         line["read_floor"] = read_floor
     if packed is not None:
         line["packed_weights"] = packed
+    if others is not None:
+        line["workloads"] = others
     props = torch.cuda.get_device_properties(0)
     line["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                       "compute_units": props.multi_processor_count,
