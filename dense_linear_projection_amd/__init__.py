@@ -17,8 +17,9 @@ for fp32 weights held as a bf16 high/low pair ``proj_prepare_hilo``,
 weights registered in the packed tile layout ``proj_packed_bytes``,
 ``proj_pack_weights``, ``proj_run_packed``, ``proj_get_plan_packed``,
 ``proj_num_candidates_packed``, ``proj_candidate_name_packed``,
-``proj_run_candidate_packed``, and the measured read floor
-``proj_read_probe``.
+``proj_run_candidate_packed``, the measured read floor
+``proj_read_probe``, and ``proj_run_noalloc`` (proj_run with no device
+allocation).
 """
 from __future__ import annotations
 
@@ -45,7 +46,7 @@ EXPORTS = ["proj_create", "proj_run", "proj_tune", "proj_destroy", "proj_status_
            "proj_prepare_hilo", "proj_run_hilo", "proj_get_plan_hilo", "proj_num_candidates_hilo",
            "proj_candidate_name_hilo", "proj_run_candidate_hilo", "proj_packed_bytes", "proj_pack_weights",
            "proj_run_packed", "proj_get_plan_packed", "proj_num_candidates_packed", "proj_candidate_name_packed",
-           "proj_run_candidate_packed", "proj_read_probe"]
+           "proj_run_candidate_packed", "proj_read_probe", "proj_run_noalloc"]
 
 
 class ProjError(RuntimeError):
@@ -98,6 +99,7 @@ def lib() -> ctypes.CDLL:
         "proj_candidate_name_packed": ([i64, i64, i64, ci, ci, ci, ci, ci, ctypes.c_char_p, ctypes.c_size_t], st),
         "proj_run_candidate_packed": ([vp, ci, vp, vp, ci, vp, ci, i64, i64, i64, vp, ci, vp], st),
         "proj_read_probe": ([vp, vp, ctypes.c_size_t, vp], st),
+        "proj_run_noalloc": (run_args, st),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -207,6 +209,15 @@ def proj_run(ctx, X, W, bias, epilogue, Y, M=None, N=None, K=None, out_dtype=Non
     M, N, K = _shape(X, W, M, N, K)
     _check(lib().proj_run(ctx, _ptr(X), _ptr(W), _ptr(bias), int(epilogue), M, N, K, _ptr(Y),
                           _out_dtype(Y, out_dtype), _stream(stream)), ctx)
+
+
+def proj_run_noalloc(ctx, X, W, bias, epilogue, Y, M=None, N=None, K=None, out_dtype=None, stream=None) -> None:
+    """proj_run without any device allocation: split-K partials go to the
+    library's static per-GPU scratch (2 MiB)."""
+    _check_operands(X, W, bias, Y)
+    M, N, K = _shape(X, W, M, N, K)
+    _check(lib().proj_run_noalloc(ctx, _ptr(X), _ptr(W), _ptr(bias), int(epilogue), M, N, K, _ptr(Y),
+                                  _out_dtype(Y, out_dtype), _stream(stream)), ctx)
 
 
 def proj_tune(ctx, X, W, bias, epilogue, Y, M=None, N=None, K=None, out_dtype=None, stream=None) -> None:

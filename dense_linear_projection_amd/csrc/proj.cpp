@@ -30,6 +30,17 @@
 
 using namespace proj;
 
+// Split-K partials of proj_run_noalloc live in this file-scope device array
+// instead of a context's workspace, so that call allocates nothing.  In host
+// code the array's name is only a stand-in: its device address is resolved
+// once per device with hipGetSymbolAddress (with that device current, when a
+// context is created on it), and only that address is passed to kernels.
+// Every call on one GPU shares that GPU's copy, which keeps the last call's
+// contents; nothing in it needs to start at zero (a split plan rewrites all
+// of its partials before summing them).
+static constexpr size_t kScratchBytes = size_t{2} << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
 namespace {
 
 constexpr uint32_t kMagic = 0x50524f4au;   // live context
@@ -71,6 +82,7 @@ struct Plan {
 struct proj_ctx {
     uint32_t magic;
     int device;
+    void *scratch_dev;   // device address of this device's copy of `scratch`
     int cus;             // compute units of the device
     double cu_flops;     // one CU's dense bf16 matrix rate (flop/s) at the device clock
     float *ws;           // split-K partial workspace, ws_bytes long (caller-bounded)
@@ -601,6 +613,27 @@ proj_status run_impl(proj_ctx *c, const void *X, const void *W, const void *bias
     return PROJ_OK;
 }
 
+// ---- allocation-free runs: the device address of `scratch` on each device
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on `device` (which must be current); resolved
+// on the first call per device.
+hipError_t scratch_address(int device, void **out) {
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[device]) {
+        void *ptr = nullptr;
+        hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!ptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[device] = ptr;
+    }
+    *out = g_scratch_ptr[device];
+    return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -626,6 +659,12 @@ proj_status proj_create(proj_ctx **out, int device, size_t max_workspace_bytes) 
     c->ws = nullptr;
     c->ws_bytes = 0;
     c->zeros = nullptr;
+    c->scratch_dev = nullptr;
+    if (scratch_address(device, &c->scratch_dev) != hipSuccess) {
+        (void)hipGetLastError();
+        delete c;
+        return PROJ_ERR_HIP;
+    }
     bool ok = hipMalloc(&c->zeros, kZeroBytes + kSinkBytes) == hipSuccess &&
               hipMemset(c->zeros, 0, kZeroBytes + kSinkBytes) == hipSuccess;
     if (ok && max_workspace_bytes > 0) {
@@ -654,6 +693,35 @@ proj_status proj_create(proj_ctx **out, int device, size_t max_workspace_bytes) 
 proj_status proj_run(proj_ctx *ctx, const void *X, const void *W, const void *bias, int epilogue, int64_t M,
                      int64_t N, int64_t K, void *Y, int out_dtype, void *stream) {
     return run_impl(ctx, X, W, bias, epilogue, M, N, K, Y, out_dtype, stream, false);
+}
+
+proj_status proj_run_noalloc(proj_ctx *ctx, const void *X, const void *W, const void *bias, int epilogue,
+                             int64_t M, int64_t N, int64_t K, void *Y, int out_dtype, void *stream) {
+    proj_status s = check_args(ctx, X, W, bias, epilogue, M, N, K, Y, out_dtype);
+    if (s != PROJ_OK || M == 0 || N == 0) return s;
+    DeviceGuard g(ctx->device);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const Key k = make_key(X, W, epilogue, M, N, K, out_dtype);
+    Candidate cand;
+    {
+        std::lock_guard<std::mutex> lock(ctx->mu);
+        auto it = ctx->plans.find(k);
+        // the plan proj_run runs for this shape, or (none cached yet) the
+        // default plan among those whose partials fit the scratch, not cached
+        cand = it != ctx->plans.end()
+                   ? it->second.cand
+                   : default_candidate(k, std::min(ctx->ws_bytes, kScratchBytes), ctx->cus);
+    }
+    if (workspace_bytes(cand, k) > kScratchBytes) {
+        set_err(ctx, "%s writes %zu bytes of split-K partials; proj_run_noalloc's static scratch holds %zu",
+                cand.name.c_str(), workspace_bytes(cand, k), kScratchBytes);
+        return PROJ_ERR_NO_MEMORY;
+    }
+    Args a = make_args(ctx, X, W, bias, epilogue, M, N, K, Y, out_dtype);
+    a.ws = static_cast<float *>(ctx->scratch_dev);
+    hipError_t e = launch(cand, a, st);
+    if (e != hipSuccess) return hip_fail(ctx, "launch", e);
+    return PROJ_OK;
 }
 
 proj_status proj_tune(proj_ctx *ctx, const void *X, const void *W, const void *bias, int epilogue, int64_t M,

@@ -140,6 +140,23 @@ proj_status proj_run(proj_ctx *ctx, const void *X, const void *W, const void *bi
                      int epilogue, int64_t M, int64_t N, int64_t K, void *Y,
                      int out_dtype, void *stream);
 
+/* proj_run for callers that cannot allocate device memory: code recorded
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, validation and result as proj_run; it runs the
+ * plan cached for the shape in ctx (tuned or default), or, when none is
+ * cached, the default plan among those whose partials fit the scratch below
+ * (not cached, never timed).  It allocates no device memory and never
+ * synchronises: a plan that splits K writes its fp32 partials to a static
+ * device array of the library, 2 MiB per GPU (held from the first context on
+ * that GPU until the process ends), instead of the context's workspace.
+ * Returns PROJ_ERR_NO_MEMORY (nothing enqueued) if the plan's partials,
+ * S * M * N * 4 bytes, exceed 2 MiB.  Every call on one GPU shares that
+ * array, so proj_run_noalloc calls whose kernels may overlap on one GPU
+ * (different streams, any contexts) race on it; order them. */
+proj_status proj_run_noalloc(proj_ctx *ctx, const void *X, const void *W, const void *bias,
+                             int epilogue, int64_t M, int64_t N, int64_t K, void *Y,
+                             int out_dtype, void *stream);
+
 /* Measure the candidates for this shape key now and cache the winner, as
  * the first uncaptured proj_run does (also re-tunes a key that holds a
  * default plan).  Returns PROJ_ERR_NOT_TUNED while `stream` is capturing. */
