@@ -686,6 +686,103 @@ __device__ __forceinline__ void stage_tile16_bf16(uint16_t *t16, const f32x4 (&a
     }
 }
 
+// Chunk position of W row r on 128-byte LDS rows for the DIRECT persistent
+// kernel.  One of its fragment reads gives 16 lanes the rows
+// 8 q + 4 j + t (q, t = 0..3; j fixed) of a 32-row pair: bits 0, 1, 3, 4
+// vary.  Rows of each parity (bit 0) must sit at 8 distinct positions of the
+// 256-byte bank window (see swz128), so the XOR takes bits 1, 3 and 4.
+__device__ __forceinline__ int swz_w(int row) { return ((row >> 1) & 1) | ((row >> 2) & 6); }
+
+// W row (within a 32-row pair) that operand row r of block j of the pair
+// reads in the DIRECT persistent kernel.
+__device__ __forceinline__ int pair_row(int r, int j) { return 8 * (r >> 2) + 4 * j + (r & 3); }
+
+// bf16 number q (0..7) of eight packed in a 16-byte vector, as fp32
+__device__ __forceinline__ float bf16_at(const u32x4 &v, int q) {
+    const uint32_t w = v[q >> 1];
+    return __uint_as_float((q & 1) ? (w & 0xffff0000u) : (w << 16));
+}
+
+// Epilogue of the DIRECT persistent kernel, straight from registers.  Block
+// (i, j) of acc holds token rows mrow0 + 16 i + (lane % 16) and, over a pair
+// of blocks (2 jp, 2 jp + 1), output features ncol0 + 32 jp + 8 fg .. +7
+// (fg = lane / 16): acc[i][2 jp][0..3] then acc[i][2 jp + 1][0..3].  With
+// S > 1 the fp32 partial of this K split goes to the workspace; otherwise
+// bias, GELU and the output rounding are applied and the 8 outputs are
+// written with one 16-byte store (bf16) or two (fp32) where the row holds
+// them whole and aligned, element by element at the ragged edges.
+template <int FM, int FN>
+__device__ __forceinline__ void direct_epilogue(const Args &a, const f32x4 (&acc)[FM][FN],
+                                                const u32x4 (&biasp)[FN / 2], int S, int split, int64_t mrow0,
+                                                int64_t ncol0, int fr, int fg) {
+    const int64_t M = a.M, N = a.N;
+    if (S > 1) {
+        float *ws = a.ws + static_cast<int64_t>(split) * M * N;
+        const bool vec = N % 4 == 0;  // the workspace is 256-byte aligned and n a multiple of 8
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int64_t m = mrow0 + i * 16 + fr;
+#pragma unroll
+            for (int jp = 0; jp < FN / 2; ++jp) {
+                const int64_t n = ncol0 + jp * 32 + 8 * fg;
+                if (m >= M || n >= N) continue;
+                float *dst = ws + m * N + n;
+                if (vec && n + 8 <= N) {
+                    __builtin_nontemporal_store(acc[i][2 * jp], reinterpret_cast<f32x4 *>(dst));
+                    __builtin_nontemporal_store(acc[i][2 * jp + 1], reinterpret_cast<f32x4 *>(dst + 4));
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (n + e < N) dst[e] = e < 4 ? acc[i][2 * jp][e] : acc[i][2 * jp + 1][e - 4];
+                }
+            }
+        }
+        return;
+    }
+    const bool yal = reinterpret_cast<uintptr_t>(a.Y) % 16 == 0;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int64_t m = mrow0 + i * 16 + fr;
+#pragma unroll
+        for (int jp = 0; jp < FN / 2; ++jp) {
+            const int64_t n = ncol0 + jp * 32 + 8 * fg;
+            if (m >= M || n >= N) continue;
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                v[e] = e < 4 ? acc[i][2 * jp][e] : acc[i][2 * jp + 1][e - 4];
+                if (a.epi & 1) v[e] += bf16_at(biasp[jp], e);
+            }
+            if (a.epi & 2) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = gelu_tanh_fast(v[e]);
+            }
+            if (a.out == OUT_BF16) {
+                uint16_t *y = static_cast<uint16_t *>(a.Y) + m * N + n;
+                if (yal && N % 8 == 0 && n + 8 <= N) {
+                    const u32x4 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                                      pack_bf16x2(v[6], v[7])};
+                    __builtin_nontemporal_store(pk, reinterpret_cast<u32x4 *>(y));
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (n + e < N) y[e] = f32_to_bf16_bits(v[e]);
+                }
+            } else {
+                float *y = static_cast<float *>(a.Y) + m * N + n;
+                if (yal && N % 4 == 0 && n + 8 <= N) {
+                    __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4 *>(y));
+                    __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]}, reinterpret_cast<f32x4 *>(y + 4));
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (n + e < N) y[e] = v[e];
+                }
+            }
+        }
+    }
+}
+
 // Persistent form of gemm_pp64_kernel: one workgroup per CU walks tiles
 // blockIdx.x, blockIdx.x + gridDim.x, ...  The LDS ring runs on across tiles
 // (the copies the last k-ranges of a tile would make past K fetch the next
@@ -703,7 +800,20 @@ __device__ __forceinline__ void stage_tile16_bf16(uint16_t *t16, const f32x4 (&a
 // Matrix ops are 16x16x32 (each wave 4 x BN/32 blocks of 16 x 16, one
 // fragment per 16 rows and k-step): with the same LDS traffic this form ran
 // 6% faster than 32x32x16 blocks on the M=4096, K=N=8192 GEMM.
-template <int BN, int GM>
+//
+// DIRECT (family gemmpp64d): the matrix op takes the W fragment as its first
+// operand and the X fragment as its second, so a 16 x 16 block holds Y
+// transposed: a lane holds one token row (lane % 16) and four output
+// features.  The 16 W rows of the two blocks of each 32-feature pair are
+// taken in the order 8 (r / 4) + 4 j + r % 4 (r the operand row, j the block
+// of the pair), so a lane holds 8 consecutive features of its row:
+// features 8 (lane / 16) .. +7 of the pair.  The epilogue then adds the
+// bias, applies GELU and stores those 8 outputs as one 16-byte store (bf16)
+// straight from registers -- no staging through LDS and no barrier, so the
+// next tile's first k-ranges (already in flight) start right after.  W rows
+// are then read 16 at a time in that order, so W's chunks are placed by
+// swz_w (below) instead of swz128 to stay free of bank conflicts.
+template <int BN, int GM, bool DIRECT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_pp64p_kernel(Args a, int S) {
     constexpr int BM = 256, NW = 8, SLOTS = 5, SLOT = 32 * 1024;
     constexpr int TM = 64, TN = BN / 2;
@@ -783,7 +893,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int j = 0; j < NCB; ++j) {
             const int b = grp * (B_BLK / 2) + wg + 4 * j;
             const int row = b * 8 + drow;
-            dma16_buf(r, static_cast<uint32_t>(row * K * 2 + ((lane & 7) ^ swz128(row)) * 16), soff,
+            const int sz = DIRECT ? swz_w(row) : swz128(row);
+            dma16_buf(r, static_cast<uint32_t>(row * K * 2 + ((lane & 7) ^ sz) * 16), soff,
                       lds + slot * SLOT + b * 1024);
         }
     };
@@ -795,6 +906,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     auto frag = [&](const char *base, int row0, int p) -> bf16x8 {
         return *reinterpret_cast<const bf16x8 *>(base + (row0 + fr) * ROWB + (((4 * p + fg) ^ sw) << 4));
     };
+    // DIRECT: block j of the wave's W rows (pair j / 2, block j % 2 of it)
+    auto frag_w = [&](const char *base, int j, int p) -> bf16x8 {
+        const int row = wn * TN + (j >> 1) * 32 + pair_row(fr, j & 1);
+        return *reinterpret_cast<const bf16x8 *>(base + row * ROWB + (((4 * p + fg) ^ swz_w(row)) << 4));
+    };
+    static_assert(!DIRECT || FN % 2 == 0, "DIRECT takes W blocks in pairs");
 
     int64_t item = blockIdx.x;
     __amdgpu_buffer_rsrc_t ca, cb, na, nb;
@@ -816,11 +933,38 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         int kb, ke;
         krange(remap(item), kb, ke);
         const int split = static_cast<int>(remap(item) % S);
-        float bias[FN];
+        // bias of this lane's output features: column j * 16 + fr of block
+        // j, or (DIRECT) features 8 fg .. +7 of pair jp as packed bf16
+        constexpr int NB = DIRECT ? 1 : FN;
+        constexpr int NBP = DIRECT ? FN / 2 : 1;
+        float bias[NB];
+        u32x4 biasp[NBP];
+        if constexpr (!DIRECT) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int64_t n = n0 + wn * TN + j * 16 + fr;
-            bias[j] = ((a.epi & 1) && n < N) ? bf16_bits_to_f32(a.bias[n]) : 0.f;
+            for (int j = 0; j < FN; ++j) {
+                const int64_t n = n0 + wn * TN + j * 16 + fr;
+                bias[j] = ((a.epi & 1) && n < N) ? bf16_bits_to_f32(a.bias[n]) : 0.f;
+            }
+        } else {
+            const bool vec = (reinterpret_cast<uintptr_t>(a.bias) % 16) == 0;
+#pragma unroll
+            for (int jp = 0; jp < FN / 2; ++jp) {
+                const int64_t n = n0 + wn * TN + jp * 32 + 8 * fg;
+                if (!(a.epi & 1) || n >= N) {
+                    biasp[jp] = u32x4{0u, 0u, 0u, 0u};
+                } else if (vec && n + 8 <= N) {
+                    biasp[jp] = *reinterpret_cast<const u32x4 *>(a.bias + n);
+                } else {
+                    uint32_t w[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint32_t lo = n + 2 * q < N ? a.bias[n + 2 * q] : 0u;
+                        const uint32_t hi = n + 2 * q + 1 < N ? a.bias[n + 2 * q + 1] : 0u;
+                        w[q] = lo | (hi << 16);
+                    }
+                    biasp[jp] = u32x4{w[0], w[1], w[2], w[3]};
+                }
+            }
         }
         f32x4 acc[FM][FN];
 #pragma unroll
@@ -839,7 +983,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                     for (int i = 0; i < FM; ++i) af[i] = frag(sa, wm * TM + i * 16, p);
 #pragma unroll
-                    for (int j = 0; j < FN; ++j) bfr[j] = frag(sb, wn * TN + j * 16, p);
+                    for (int j = 0; j < FN; ++j) bfr[j] = DIRECT ? frag_w(sb, j, p) : frag(sb, wn * TN + j * 16, p);
                     if (p == 0) {
                         // B(T+1): this item's, or the next item's first
                         if (T + 1 < ke)
@@ -863,7 +1007,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                     for (int i = 0; i < FM; ++i)
 #pragma unroll
-                        for (int j = 0; j < FN; ++j) acc[i][j] = mfma16x16x32(af[i], bfr[j], acc[i][j]);
+                        for (int j = 0; j < FN; ++j)
+                            acc[i][j] = DIRECT ? mfma16x16x32(bfr[j], af[i], acc[i][j])
+                                               : mfma16x16x32(af[i], bfr[j], acc[i][j]);
                     if (GRP == 0 && p == 1) wait_vm<NCA>();
                     barrier_nofence();
                 }
@@ -876,6 +1022,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         else
             run(std::integral_constant<int, 1>{});
 
+        if constexpr (DIRECT) {
+            direct_epilogue<FM, FN>(a, acc, biasp, S, split, m0 + wm * TM, n0 + wn * TN, fr, fg);
+        } else {
         // ---- epilogue.  The slots of the last k-range's A and B (s0 + 3,
         // s0 + 4) are free once every wave's reads of it have landed; the
         // next tile's A(0), B(0), A(1) are in the other three.
@@ -948,6 +1097,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     }
             }
         }
+        }
         ca = na;
         cb = nb;
         resources(item + 2 * static_cast<int64_t>(gridDim.x), na, nb, nkb);
@@ -975,7 +1125,9 @@ PROJ_GEMM_PP_VARIANTS(PROJ_GEMM_PP_INST)
 #define PROJ_GEMM_PP64_VARIANTS(X) X(256, 4) X(256, 8) X(192, 4)
 #define PROJ_GEMM_PP64_INST(BN, GM) template __global__ void gemm_pp64_kernel<BN, GM>(Args);
 PROJ_GEMM_PP64_VARIANTS(PROJ_GEMM_PP64_INST)
-#define PROJ_GEMM_PP64P_INST(BN, GM) template __global__ void gemm_pp64p_kernel<BN, GM>(Args, int);
+#define PROJ_GEMM_PP64P_INST(BN, GM)                                          \
+    template __global__ void gemm_pp64p_kernel<BN, GM, false>(Args, int); \
+    template __global__ void gemm_pp64p_kernel<BN, GM, true>(Args, int);
 PROJ_GEMM_PP64_VARIANTS(PROJ_GEMM_PP64P_INST)
 
 #ifndef __HIP_DEVICE_COMPILE__
@@ -1041,20 +1193,20 @@ static hipError_t launch_gemm_pp64(const Args &a, int S, hipStream_t st) {
 // kernel launches one workgroup per CU)
 static int g_num_cus = 0;
 
-template <int BN, int GM>
+template <int BN, int GM, bool DIRECT>
 static hipError_t prepare_gemm_pp64p() {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&g_num_cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    auto fn = gemm_pp64p_kernel<BN, GM>;
+    auto fn = gemm_pp64p_kernel<BN, GM, DIRECT>;
     return hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
                                5 * 32 * 1024);
 }
 
 // K < 128 (one k-range) runs the non-persistent kernel; S > 1 splits K into
 // S parts of at least two k-ranges each and adds the reduction pass
-template <int BN, int GM>
+template <int BN, int GM, bool DIRECT>
 static hipError_t launch_gemm_pp64p(const Args &a, int S, hipStream_t st) {
     if (a.wpack || (a.kx != a.K && (a.kx % 64 != 0 || a.K < 128))) return hipErrorInvalidValue;
     if (a.K < 128) return S == 1 ? launch_gemm_pp64<BN, GM>(a, 1, st) : hipErrorInvalidValue;
@@ -1063,7 +1215,7 @@ static hipError_t launch_gemm_pp64p(const Args &a, int S, hipStream_t st) {
     if (G <= 0 || G > 0x7fffffff) return hipErrorInvalidConfiguration;
     const int64_t cus = g_num_cus > 0 ? g_num_cus : 256;
     const int64_t grid = G < cus ? G : cus;
-    hipLaunchKernelGGL((gemm_pp64p_kernel<BN, GM>), dim3(static_cast<unsigned>(grid)), dim3(512), 5 * 32 * 1024, st, a,
+    hipLaunchKernelGGL((gemm_pp64p_kernel<BN, GM, DIRECT>), dim3(static_cast<unsigned>(grid)), dim3(512), 5 * 32 * 1024, st, a,
                        S);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || S == 1) return e;
@@ -1077,10 +1229,13 @@ static hipError_t launch_gemm_pp64p(const Args &a, int S, hipStream_t st) {
 #define PROJ_GEMM_PP64_ENTRY(BN, GM) \
     {"gemmpp64", 256, BN, 64, 64, 4, 2, GM, kRingMaxK, 1, &launch_gemm_pp64<BN, GM>, &prepare_gemm_pp64<BN, GM>},
 #define PROJ_GEMM_PP64P_ENTRY(BN, GM) \
-    {"gemmpp64p", 256, BN, 64, 64, 4, 2, GM, kRingMaxK, 16, &launch_gemm_pp64p<BN, GM>, &prepare_gemm_pp64p<BN, GM>},
+    {"gemmpp64p", 256, BN, 64, 64, 4, 2, GM, kRingMaxK, 16, &launch_gemm_pp64p<BN, GM, false>, &prepare_gemm_pp64p<BN, GM, false>},
+#define PROJ_GEMM_PP64D_ENTRY(BN, GM) \
+    {"gemmpp64d", 256, BN, 64, 64, 4, 2, GM, kRingMaxK, 16, &launch_gemm_pp64p<BN, GM, true>, &prepare_gemm_pp64p<BN, GM, true>},
 const GemmVariant kGemmVariants[] = {PROJ_GEMM_VARIANTS(PROJ_GEMM_ENTRY) PROJ_GEMM_PP_VARIANTS(PROJ_GEMM_PP_ENTRY)
                                          PROJ_GEMM_PP64_VARIANTS(PROJ_GEMM_PP64_ENTRY)
-                                             PROJ_GEMM_PP64_VARIANTS(PROJ_GEMM_PP64P_ENTRY)};
+                                             PROJ_GEMM_PP64_VARIANTS(PROJ_GEMM_PP64P_ENTRY)
+                                                 PROJ_GEMM_PP64_VARIANTS(PROJ_GEMM_PP64D_ENTRY)};
 const int kNumGemmVariants = sizeof(kGemmVariants) / sizeof(kGemmVariants[0]);
 #endif
 

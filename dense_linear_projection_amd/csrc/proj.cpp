@@ -248,8 +248,10 @@ std::vector<Candidate> candidates(const Key &k) {
         for (int i = 0; i < kNumGemmVariants; ++i) {
             const GemmVariant &v = kGemmVariants[i];
             if (k.K % v.kmult != 0) continue;
-            // the persistent kernel is the GEMM that reads a hi/lo pair
-            if (k.hilo && (std::strcmp(v.family, "gemmpp64p") != 0 || (k.K / 2) % 64 != 0 || k.K < 128)) continue;
+            // the persistent kernels are the GEMMs that read a hi/lo pair
+            if (k.hilo && ((std::strcmp(v.family, "gemmpp64p") != 0 && std::strcmp(v.family, "gemmpp64d") != 0) ||
+                           (k.K / 2) % 64 != 0 || k.K < 128))
+                continue;
             if (v.kmax > 0 && k.K > v.kmax) continue;
             out.push_back({KIND_GEMM, i, 1, gemm_name(v, 1)});
             // K splits: at least two 64-wide k-ranges each
