@@ -25,6 +25,7 @@ struct Args {
     int64_t kx;            // X row length: K, or K/2 for a hi/lo weight pair (X column k' reads k' mod kx)
     int epi, out;
     int wpack = 0;         // 0: W row-major [N][K]; t > 0: W packed in tiles of 16t rows (see proj_pack_weights)
+    int atomic = 0;        // split K (S > 1), fp32 Y: partials are added into Y (zeroed first) with fp32 atomics
     float *ws;             // split-K partials [S][M][N] (library-owned)
     const uint16_t *zeros; // >= 64 zero bytes in device memory, for masked loads
 };

@@ -69,6 +69,7 @@ struct Candidate {
     int variant;  // index into the kernel table
     int splits;   // K ranges over workgroups (1: no split)
     std::string name;
+    int atomic = 0;  // splits added into a zeroed fp32 Y with atomics instead of a workspace pass
 };
 
 struct Plan {
@@ -150,12 +151,16 @@ int mt_for(int64_t M) {
     return need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 0;
 }
 
-std::string stream_name(const StreamVariant &v, int S) {
+std::string stream_name(const StreamVariant &v, int S, bool atomic = false) {
     char b[96];
-    snprintf(b, sizeof b, "stream_mt%d_nt%d_w%d_k%d_d%d%s_s%d", v.mt, v.nt, v.waves, v.kc, v.depth,
-             v.wnt ? "_wnt" : "", S);
+    snprintf(b, sizeof b, "stream_mt%d_nt%d_w%d_k%d_d%d%s_s%d%s", v.mt, v.nt, v.waves, v.kc, v.depth,
+             v.wnt ? "_wnt" : "", S, atomic ? "_atomic" : "");
     return b;
 }
+
+// Split partials may be added into Y with fp32 atomics when Y is fp32 and
+// the epilogue is additive (no GELU): the bias is then added by one split.
+bool atomic_ok(const Key &k) { return k.out == PROJ_OUT_F32 && !(k.epi & 2); }
 
 std::string gemv_name(const GemvVariant &v, int S) {
     char b[96];
@@ -196,6 +201,7 @@ std::vector<Candidate> candidates(const Key &k) {
                 if (S > 1 && S > stages) continue;
                 if (mblocks * tiles * S > 0x7fffffff) continue;
                 out.push_back({KIND_STREAM, i, S, stream_name(v, S)});
+                if (S > 1 && atomic_ok(k)) out.push_back({KIND_STREAM, i, S, stream_name(v, S, true), 1});
             }
         }
         return out;
@@ -226,6 +232,7 @@ std::vector<Candidate> candidates(const Key &k) {
                     if (S > 1 && S > stages) continue;
                     if (mblocks * tiles * S > 0x7fffffff) continue;
                     out.push_back({KIND_STREAM, i, S, stream_name(v, S)});
+                    if (S > 1 && atomic_ok(k)) out.push_back({KIND_STREAM, i, S, stream_name(v, S, true), 1});
                 }
             }
         }
@@ -269,7 +276,7 @@ std::vector<Candidate> candidates(const Key &k) {
 
 // Bytes of fp32 partials a candidate writes to the split-K workspace.
 size_t workspace_bytes(const Candidate &c, const Key &k) {
-    if (c.splits <= 1) return 0;
+    if (c.splits <= 1 || c.atomic) return 0;
     return static_cast<size_t>(c.splits) * static_cast<size_t>(k.M) * static_cast<size_t>(k.N) * sizeof(float);
 }
 
@@ -345,7 +352,11 @@ Args make_args(proj_ctx *c, const void *X, const void *W, const void *bias, int 
 hipError_t launch(const Candidate &cand, const Args &a, hipStream_t st) {
     switch (cand.kind) {
         case KIND_GEMM: return kGemmVariants[cand.variant].launch(a, cand.splits, st);
-        case KIND_STREAM: return kStreamVariants[cand.variant].launch(a, cand.splits, st);
+        case KIND_STREAM: {
+            Args b = a;
+            b.atomic = cand.atomic;
+            return kStreamVariants[cand.variant].launch(b, cand.splits, st);
+        }
         case KIND_GEMV: return kGemvVariants[cand.variant].launch(a, cand.splits, st);
         default: return launch_generic(a, st);
     }

@@ -36,6 +36,13 @@
 //   * optionally (WNT) the W copies carry the non-temporal cache hint: W is
 //     read once, and streaming it past L2 keeps the X rows, which every
 //     workgroup re-reads, resident there (it pays when X is large, M = 64);
+//   * with S > 1 and fp32 output the partials may instead be added straight
+//     into Y with fp32 atomics (a.atomic), Y having been zeroed by a small
+//     kernel first, the bias added by split 0 only: no workspace and no
+//     second pass over it (the worklog's atomic accumulation, section "Could
+//     I avoid reading all those router partials back?"); the order of the
+//     additions then varies from run to run, so the result is correct within
+//     rounding, not bit-reproducible, unless every sum is exact;
 //   * workgroups walk their stages starting at a tile-dependent rotation, so
 //     at any moment the machine's reads are spread over all of K rather than
 //     all hitting the same column offset of every power-of-two-strided row.
@@ -270,6 +277,9 @@ __global__ __launch_bounds__(WAVES * 64) void stream_kernel(Args a, int S) {
         if (S == 1) {
             const float b = (a.epi & 1) ? bf16_bits_to_f32(bias[n]) : 0.f;
             store_out(a.Y, a.out, (m0 + m) * N + n, apply_epilogue(s, a.epi, b));
+        } else if (a.atomic) {
+            const float b = (split == 0 && (a.epi & 1)) ? bf16_bits_to_f32(bias[n]) : 0.f;
+            unsafeAtomicAdd(static_cast<float *>(a.Y) + (m0 + m) * N + n, s + b);
         } else {
             a.ws[(static_cast<int64_t>(split) * a.M + m0 + m) * N + n] = s;
         }
@@ -287,6 +297,14 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(Args a, int S) {
     const int64_t n = idx % a.N;
     const float b = (a.epi & 1) ? bf16_bits_to_f32(a.bias[n]) : 0.f;
     store_out(a.Y, a.out, idx, apply_epilogue(s, a.epi, b));
+}
+
+// Y = 0 before the atomic split-K accumulation (a kernel rather than a
+// memset, so that a captured graph replays it as an ordinary kernel node).
+__global__ __launch_bounds__(256) void zero_f32_kernel(float *y, int64_t n) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * 256)
+        y[i] = 0.f;
 }
 
 // ---------------------------------------------------------------- registry
@@ -332,10 +350,20 @@ static hipError_t launch_stream(const Args &a, int S, hipStream_t st) {
     // it is also the only one that reads a hi/lo pair's X (kx < K), whose
     // wrap must fall on a stage boundary
     const int64_t rows_x = a.M < 16 * MT ? a.M : 16 * MT;  // X rows one workgroup addresses
+    // atomic accumulation: split K, fp32 output, no GELU (it is not additive)
+    if (a.atomic && (S < 2 || a.out != OUT_F32 || (a.epi & 2))) return hipErrorInvalidValue;
     const bool fast = a.K % KC == 0 && a.kx % KC == 0 && rows_x * a.kx * 2 < (int64_t{1} << 32) &&
                       16 * NT * a.K * 2 < (int64_t{1} << 32);
     if (!fast && a.kx != a.K) return hipErrorInvalidValue;
     if (a.wpack && (a.wpack != NT || !fast || KC % 128 != 0)) return hipErrorInvalidValue;
+    if (a.atomic) {
+        const int64_t n = a.M * a.N;
+        const int64_t blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
+        hipLaunchKernelGGL(zero_f32_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
+                           static_cast<float *>(a.Y), n);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     if (fast)
         hipLaunchKernelGGL((stream_kernel<MT, NT, WV, KC, D, WNT, true>), dim3(static_cast<unsigned>(grid)),
                            dim3(WV * 64), lds_bytes, st, a, S);
@@ -343,7 +371,7 @@ static hipError_t launch_stream(const Args &a, int S, hipStream_t st) {
         hipLaunchKernelGGL((stream_kernel<MT, NT, WV, KC, D, WNT, false>), dim3(static_cast<unsigned>(grid)),
                            dim3(WV * 64), lds_bytes, st, a, S);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || S == 1) return e;
+    if (e != hipSuccess || S == 1 || a.atomic) return e;
     return launch_splitk_reduce(a, S, st);
 }
 
