@@ -92,6 +92,7 @@ struct proj_ctx {
     std::map<Key, Plan> plans;
     std::mutex mu;
     std::string err;
+    std::string dev_id;  // architecture and CU count: the plan file's device key
 };
 
 // A captured graph keeps the context's workspace and zero page as kernel
@@ -106,6 +107,59 @@ struct proj_graph {
 };
 
 namespace {
+
+bool env_flag(const char *name, bool dflt);
+
+// ---- optional plan file and log.  PROJ_PLAN_FILE names a text file of
+// measured plans: each tuned plan is appended as one line
+//   proj-plan 1 <device> <M> <N> <K> <epi> <out> <aligned> <hilo> <wpack> <plan> <us>
+// and proj_create loads the lines of its device (architecture and CU
+// count), the last line of a key winning, so a later process or context
+// starts from the measured plans instead of tuning again.  A line whose plan
+// is not a candidate of its key (another library build), or whose partials
+// do not fit the context's workspace, is skipped.  PROJ_LOG=1 prints each
+// plan decision to stderr.
+bool plan_log() { return env_flag("PROJ_LOG", false); }
+
+void save_plan(const proj_ctx *c, const Key &k, const Plan &p) {
+    const char *path = std::getenv("PROJ_PLAN_FILE");
+    if (!path || !*path) return;
+    FILE *f = std::fopen(path, "a");
+    if (!f) return;
+    std::fprintf(f, "proj-plan 1 %s %lld %lld %lld %d %d %d %d %d %s %.3f\n", c->dev_id.c_str(), (long long)k.M,
+                 (long long)k.N, (long long)k.K, k.epi, k.out, k.aligned, k.hilo, k.wpack, p.cand.name.c_str(), p.us);
+    std::fclose(f);
+}
+
+std::vector<Candidate> candidates(const Key &k);
+bool fits(const Candidate &c, const Key &k, size_t ws);
+
+int load_plans(proj_ctx *c) {
+    const char *path = std::getenv("PROJ_PLAN_FILE");
+    if (!path || !*path) return 0;
+    FILE *f = std::fopen(path, "r");
+    if (!f) return 0;
+    char line[512], dev[128], name[160];
+    int loaded = 0;
+    while (std::fgets(line, sizeof line, f)) {
+        long long M, N, K;
+        int ver, epi, out, al, hilo, wpack;
+        float us;
+        if (std::sscanf(line, "proj-plan %d %127s %lld %lld %lld %d %d %d %d %d %159s %f", &ver, dev, &M, &N, &K, &epi,
+                        &out, &al, &hilo, &wpack, name, &us) != 12 ||
+            ver != 1 || c->dev_id != dev || M <= 0 || N <= 0 || K < 0)
+            continue;
+        const Key k{M, N, K, epi, out, al, hilo, wpack};
+        for (const Candidate &cand : candidates(k))
+            if (cand.name == name && fits(cand, k, c->ws_bytes)) {
+                c->plans[k] = Plan{cand, true, us};
+                ++loaded;
+                break;
+            }
+    }
+    std::fclose(f);
+    return loaded;
+}
 
 bool env_flag(const char *name, bool dflt) {
     const char *v = std::getenv(name);
@@ -255,10 +309,11 @@ std::vector<Candidate> candidates(const Key &k) {
         for (int i = 0; i < kNumGemmVariants; ++i) {
             const GemmVariant &v = kGemmVariants[i];
             if (k.K % v.kmult != 0) continue;
-            // the persistent kernels are the GEMMs that read a hi/lo pair
-            if (k.hilo && ((std::strcmp(v.family, "gemmpp64p") != 0 && std::strcmp(v.family, "gemmpp64d") != 0) ||
-                           (k.K / 2) % 64 != 0 || k.K < 128))
-                continue;
+            // the persistent kernels (families gemmpp64p*, gemmpp64d*) are the
+            // GEMMs that read a hi/lo pair
+            const bool persistent = std::strncmp(v.family, "gemmpp64", 8) == 0 &&
+                                    (v.family[8] == 'p' || v.family[8] == 'd');
+            if (k.hilo && (!persistent || (k.K / 2) % 64 != 0 || k.K < 128)) continue;
             if (v.kmax > 0 && k.K > v.kmax) continue;
             out.push_back({KIND_GEMM, i, 1, gemm_name(v, 1)});
             // K splits: at least two 64-wide k-ranges each
@@ -554,15 +609,76 @@ proj_status tune(proj_ctx *c, const Key &k, const Args &a, hipStream_t st, Plan 
         return PROJ_ERR_HIP;
     }
     // pass 2: the leaders again, interleaved round by round so that clock
-    // and thermal drift over the tuning run falls on all of them alike
+    // and thermal drift over the tuning run falls on all of them alike.
+    // Where P >= 2 copies of the operands fill at least half the flush
+    // buffer (more than the last-level cache), each leader is timed as a
+    // model replays it: a HIP graph of P calls cycling over the copies, so
+    // every call reads its operands from HBM and back-to-back kernels
+    // (split-K passes, zero fills) run with graph launch gaps.  Single cold
+    // launches carry a launch overhead of their own that reorders plans of a
+    // few microseconds.  Otherwise the leaders are timed as in pass 1.
     std::sort(ranked.begin(), ranked.end());
-    const size_t lead = ranked.size() < 4 ? ranked.size() : 4;
+    auto up256 = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t xb = static_cast<size_t>(a.M) * static_cast<size_t>(a.kx) * 2;
+    const size_t wb = a.wpack ? static_cast<size_t>(proj_packed_bytes(a.N, a.K, a.wpack))
+                              : static_cast<size_t>(a.N) * static_cast<size_t>(a.K) * 2;
+    const size_t bb = (a.epi & 1) ? static_cast<size_t>(a.N) * 2 : 0;
+    const size_t set = up256(xb) + up256(wb) + up256(bb);
+    const size_t P = (fbuf && st && set > 0) ? std::min<size_t>(256, kFlushBytes / set) : 0;
+    const bool graphs = P >= 2 && P * set >= kFlushBytes / 2;
+    const size_t lead = std::min(ranked.size(), graphs ? size_t{8} : size_t{4});
     std::vector<std::vector<float>> t2(lead);
-    for (int r = 0; r < 15; ++r)
-        for (size_t j = 0; j < lead; ++j) {
-            const float us = time_once(ranked[j].second);
-            if (us >= 0.f) t2[j].push_back(us);
+    bool graphed = false;
+    if (graphs) {
+        std::vector<Args> sets(P, a);
+        bool ok = true;
+        for (size_t p = 0; p < P && ok; ++p) {
+            char *x = static_cast<char *>(fbuf) + p * set, *w = x + up256(xb), *b = w + up256(wb);
+            ok = hipMemcpyAsync(x, a.X, xb, hipMemcpyDeviceToDevice, st) == hipSuccess &&
+                 hipMemcpyAsync(w, a.W, wb, hipMemcpyDeviceToDevice, st) == hipSuccess &&
+                 (bb == 0 || hipMemcpyAsync(b, a.bias, bb, hipMemcpyDeviceToDevice, st) == hipSuccess);
+            sets[p].X = reinterpret_cast<const uint16_t *>(x);
+            sets[p].W = reinterpret_cast<const uint16_t *>(w);
+            if (bb) sets[p].bias = reinterpret_cast<const uint16_t *>(b);
         }
+        std::vector<hipGraphExec_t> ex(lead, nullptr);
+        for (size_t j = 0; j < lead && ok; ++j) {
+            if (hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+                ok = false;
+                break;
+            }
+            bool launched = true;
+            for (size_t p = 0; p < P && launched; ++p) launched = launch(cands[ranked[j].second], sets[p], st) == hipSuccess;
+            hipGraph_t gr = nullptr;
+            const bool ended = hipStreamEndCapture(st, &gr) == hipSuccess;
+            ok = launched && ended && gr && hipGraphInstantiate(&ex[j], gr, nullptr, nullptr, 0) == hipSuccess;
+            if (gr) hipGraphDestroy(gr);
+        }
+        for (size_t j = 0; j < lead && ok; ++j) ok = hipGraphLaunch(ex[j], st) == hipSuccess;  // first replay
+        ok = ok && hipStreamSynchronize(st) == hipSuccess;
+        for (int r = 0; r < 15 && ok; ++r)
+            for (size_t j = 0; j < lead && ok; ++j) {
+                float ms = 0.f;
+                ok = hipEventRecord(e0, st) == hipSuccess && hipGraphLaunch(ex[j], st) == hipSuccess &&
+                     hipEventRecord(e1, st) == hipSuccess && hipEventSynchronize(e1) == hipSuccess &&
+                     hipEventElapsedTime(&ms, e0, e1) == hipSuccess;
+                if (ok) t2[j].push_back(ms * 1000.f / static_cast<float>(P));
+            }
+        for (hipGraphExec_t x : ex)
+            if (x) hipGraphExecDestroy(x);
+        (void)hipGetLastError();
+        graphed = ok;
+        if (!ok) {
+            hipStreamSynchronize(st);
+            for (auto &t : t2) t.clear();
+        }
+    }
+    if (!graphed)
+        for (int r = 0; r < 15; ++r)
+            for (size_t j = 0; j < lead; ++j) {
+                const float us = time_once(ranked[j].second);
+                if (us >= 0.f) t2[j].push_back(us);
+            }
     (void)hipGetLastError();
     hipEventDestroy(e0);
     hipEventDestroy(e1);
@@ -614,10 +730,18 @@ proj_status run_impl(proj_ctx *c, const void *X, const void *W, const void *bias
             s = tune(c, k, a, st, p);
             if (s != PROJ_OK) return s;
             c->plans[k] = p;
+            save_plan(c, k, p);
+            if (plan_log())
+                std::fprintf(stderr, "proj: M=%lld N=%lld K=%lld epi=%d out=%d hilo=%d wpack=%d: tuned %s %.2f us\n",
+                             (long long)M, (long long)N, (long long)K, epi, out, hilo, wpack, p.cand.name.c_str(), p.us);
             return PROJ_OK;  // tune() already left the winner's result in Y
         }
         p = Plan{default_candidate(k, c->ws_bytes, c->cus), false, 0.f};
         it = c->plans.insert_or_assign(k, p).first;
+        if (plan_log())
+            std::fprintf(stderr, "proj: M=%lld N=%lld K=%lld epi=%d out=%d hilo=%d wpack=%d: default %s (%s)\n",
+                         (long long)M, (long long)N, (long long)K, epi, out, hilo, wpack, p.cand.name.c_str(),
+                         cap ? "stream capture" : "PROJ_TUNE=0");
     } else if (force_tune) {
         // already tuned: just run it
     }
@@ -699,6 +823,13 @@ proj_status proj_create(proj_ctx **out, int device, size_t max_workspace_bytes) 
         delete c;
         return PROJ_ERR_HIP;
     }
+    c->dev_id = std::string(prop.gcnArchName) + "_cu" + std::to_string(c->cus);
+    for (char &ch : c->dev_id)
+        if (ch == ' ') ch = '_';
+    const int loaded = load_plans(c);
+    if (plan_log() && loaded)
+        std::fprintf(stderr, "proj: %d plans for %s loaded from %s\n", loaded, c->dev_id.c_str(),
+                     std::getenv("PROJ_PLAN_FILE"));
     *out = c;
     return PROJ_OK;
 }

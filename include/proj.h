@@ -47,6 +47,15 @@
  * Arguments are validated before any HIP call.  HIP failures return
  * PROJ_ERR_HIP and the message is kept in the context (proj_last_error).
  *
+ * Environment: PROJ_TUNE=0 takes untimed default plans instead of measuring
+ * (see proj_run).  PROJ_PLAN_FILE=<path> keeps measured plans in a text
+ * file: every plan a context tunes is appended as one line, keyed by the
+ * device (architecture and compute-unit count) and the shape key, and
+ * proj_create loads the lines of its device (the last line of a key wins;
+ * lines naming a plan this build does not have, or whose split-K partials
+ * do not fit the context's workspace, are skipped).  PROJ_LOG=1 prints each
+ * plan decision (tuned, default, loaded) to stderr.
+ *
  * Threading: a context holds one split-K partial workspace.  Calls that may
  * run at the same time on the GPU (different streams) must use different
  * contexts, or the caller must order them.  Host-side, a context may be used from one
