@@ -53,7 +53,9 @@ FAMILY_SOURCES = {
     "stream_kernel": ["stream.hip", "common.hpp"],
     "gemm_pp_kernel": ["gemm.hip", "common.hpp"],
     "gemm_pp64_kernel": ["gemm.hip", "common.hpp"],
+    "gemm_pp64p_kernel": ["gemm.hip", "common.hpp"],
     "gemm_kernel": ["gemm.hip", "common.hpp"],
+    "gemv_kernel": ["gemv.hip", "common.hpp"],
 }
 
 
@@ -71,38 +73,49 @@ def counters_path(workload_name: str) -> str:
 
 
 def load_traffic(workload_name: str, plan_kernel: str):
-    """HBM bytes per launch of the planned kernel, from committed rocprofv3
-    counter runs (FETCH_SIZE and WRITE_SIZE, each scaled by what the same
-    counter reads for a plain copy of known size), if they were taken on the
-    current kernel sources and include this plan; else None."""
+    """HBM bytes per launch of the planned (dominant) kernel, from committed
+    rocprofv3 counter runs (FETCH_SIZE and WRITE_SIZE, each scaled by what
+    the same counter reads for a plain copy of known size), if they were
+    taken on the current sources of that kernel's family and include this
+    plan; else None."""
     path = counters_path(workload_name)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         c = json.load(f)
-    if c.get("src_hash") != kernel_sources_hash(c["family"]):
-        return None
     entry = c.get("plans", {}).get(plan_kernel)
-    return None if entry is None else round(entry["traffic_bytes_per_launch"], 1)
+    if entry is None or entry.get("src_hash") != kernel_sources_hash(entry["family"]):
+        return None
+    return round(entry["traffic_bytes_per_launch"], 1)
 
 
-def stream_plan_launch(plan: str, w):
-    """(kernel-name part, work-items) of the launch a one-pass stream plan
-    makes on workload w, e.g. stream_mt1_nt2_w4_k128_d4_wnt_s1 ->
-    ("stream_kernel<1, 2, 4, 128, 4, 1, true>", 65536)."""
+def plan_launch(plan: str, w, cus: int = 256):
+    """(family, kernel-name part, work-items) of the dominant kernel a plan
+    launches on workload w: the streaming kernel of a stream plan (split or
+    not, atomic or not; the zero fill or split-K pass beside it is small), or
+    the GEMM kernel, e.g. stream_mt1_nt2_w4_k128_d4_wnt_s1 ->
+    ("stream_kernel", "stream_kernel<1, 2, 4, 128, 4, 1, true>", 65536)."""
     import re
-    m = re.fullmatch(r"stream_mt(\d+)_nt(\d+)_w(\d+)_k(\d+)_d(\d+)(_wnt)?_s(\d+)", plan)
-    if m is None:
-        raise SystemExit("not a stream plan: %r" % plan)
-    mt, nt, waves, kc, d = (int(m.group(i)) for i in range(1, 6))
-    wnt, S = m.group(6) is not None, int(m.group(7))
-    if S != 1:
-        raise SystemExit("counters are taken on one-pass plans only (a split plan adds a reduction kernel)")
-    fast = w.K % kc == 0  # whole stages take the buffer-resource copy path
-    name = "stream_kernel<%d, %d, %d, %d, %d, %d, %s>" % (mt, nt, waves, kc, d, int(wnt), "true" if fast else "false")
-    tiles = -(-w.N // (16 * nt))
-    mblocks = -(-w.M // (16 * mt))
-    return name, mblocks * tiles * S * waves * 64
+    m = re.fullmatch(r"stream_mt(\d+)_nt(\d+)_w(\d+)_k(\d+)_d(\d+)(_wnt)?_s(\d+)(_atomic)?", plan)
+    if m is not None:
+        mt, nt, waves, kc, d = (int(m.group(i)) for i in range(1, 6))
+        wnt, S = m.group(6) is not None, int(m.group(7))
+        fast = w.K % kc == 0  # whole stages take the buffer-resource copy path
+        name = "stream_kernel<%d, %d, %d, %d, %d, %d, %s>" % (mt, nt, waves, kc, d, int(wnt),
+                                                              "true" if fast else "false")
+        tiles = -(-w.N // (16 * nt))
+        mblocks = -(-w.M // (16 * mt))
+        return "stream_kernel", name, mblocks * tiles * S * waves * 64
+    m = re.fullmatch(r"gemmpp64([pd]?)_256x(\d+)x64_w4x2_g(\d+)(_s(\d+))?", plan)
+    if m is not None:
+        kind, bn, gm = m.group(1), int(m.group(2)), int(m.group(3))
+        S = int(m.group(5) or 1)
+        G = -(-w.M // 256) * -(-w.N // bn) * S
+        if kind == "":
+            return "gemm_pp64_kernel", "gemm_pp64_kernel<%d, %d>" % (bn, gm), G * 512
+        return ("gemm_pp64p_kernel", "gemm_pp64p_kernel<%d, %d, %s>" % (bn, gm, "true" if kind == "d" else "false"),
+                min(G, cus) * 512)
+    raise SystemExit("no counter mapping for plan %r" % plan)
 
 
 def _pmc_per_dispatch(run_dir: str, counter: str, name_part: str, skip_first: int = 0, grid: int = 0):
@@ -139,28 +152,86 @@ def ingest_counters(args) -> int:
     fetch_scale, write_scale = copy_bytes / (cfetch * 1024), copy_bytes / (cwrite * 1024)
     plans = {}
     for plan in args.plans:
-        kern, grid = stream_plan_launch(plan, w)
+        fam, kern, grid = plan_launch(plan, w)
         fetch, nf = _pmc_per_dispatch(args.ingest[0], "FETCH_SIZE", kern, grid=grid)
         write, nw = _pmc_per_dispatch(args.ingest[1], "WRITE_SIZE", kern, grid=grid)
         traffic = fetch * 1024 * fetch_scale + write * 1024 * write_scale
-        plans[plan] = {"kernel_name_part": kern, "grid_work_items": grid,
+        plans[plan] = {"family": fam, "src_files": FAMILY_SOURCES[fam], "src_hash": kernel_sources_hash(fam),
+                       "kernel_name_part": kern, "grid_work_items": grid,
                        "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
                        "dispatches": [nf, nw], "traffic_bytes_per_launch": traffic,
                        "traffic_over_alg": traffic / w.alg_bytes()}
+    # plans ingested earlier (other counter runs of the same workload) stay
+    path = counters_path(w.name)
+    if os.path.exists(path):
+        with open(path) as f:
+            old = json.load(f).get("plans", {})
+        plans = {**{k: v for k, v in old.items() if "family" in v}, **plans}
     out = {
         "workload": w.name,
         "copy_bytes": copy_bytes,
         "copy_fetch_kib": cfetch, "copy_write_kib": cwrite,
         "fetch_scale": fetch_scale, "write_scale": write_scale,
         "alg_bytes_per_launch": w.alg_bytes(),
-        "family": "stream_kernel",
-        "src_files": FAMILY_SOURCES["stream_kernel"],
-        "src_hash": kernel_sources_hash("stream_kernel"),
         "plans": plans,
     }
     with open(counters_path(w.name), "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
+    return 0
+
+
+def timeline(args) -> int:
+    """Per-call timeline of graph-replayed steps from a rocprofv3
+    --kernel-trace CSV (run_kernel_trace.csv): the kernels of each call of
+    the projection in launch order, their durations and the gaps between
+    them and to the next call, as medians over the calls that were replayed
+    back to back (a call follows the previous one within --gap-us).  The
+    calls are the dispatches of kernels whose name contains one of
+    --kernels, grouped so that each group starts with the first of those
+    names."""
+    import csv
+    rows = []
+    with open(args.timeline) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            if any(k in name for k in args.kernels):
+                rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), name))
+    rows.sort()
+    first = args.kernels[0]
+    calls, cur = [], []
+    for r in rows:
+        if first in r[2] and cur:
+            calls.append(cur)
+            cur = []
+        cur.append(r)
+    if cur:
+        calls.append(cur)
+    shape = [len(c) for c in calls]
+    n = max(set(shape), key=shape.count) if shape else 0
+    steady = []
+    for i in range(1, len(calls) - 1):
+        c, nxt, prev = calls[i], calls[i + 1], calls[i - 1]
+        if len(c) != n or (c[0][0] - prev[-1][1]) > args.gap_us * 1e3 or (nxt[0][0] - c[-1][1]) > args.gap_us * 1e3:
+            continue
+        steady.append((c, nxt[0][0]))
+    if not steady:
+        print("no back-to-back calls found", file=sys.stderr)
+        return 1
+
+    def med(xs):
+        xs = sorted(xs)
+        return xs[len(xs) // 2]
+    parts = []
+    for j in range(n):
+        parts.append({"kernel": steady[0][0][j][2][:90],
+                      "duration_us": round(med([c[j][1] - c[j][0] for c, _ in steady]) / 1e3, 3)})
+        if j + 1 < n:
+            parts.append({"gap_us": round(med([c[j + 1][0] - c[j][1] for c, _ in steady]) / 1e3, 3)})
+    parts.append({"gap_to_next_call_us": round(med([t - c[-1][1] for c, t in steady]) / 1e3, 3)})
+    per_call = med([t - c[0][0] for c, t in steady]) / 1e3
+    print(json.dumps({"calls": len(steady), "kernels_per_call": n, "per_call_us": round(per_call, 3),
+                      "timeline": parts}))
     return 0
 
 
@@ -506,7 +577,8 @@ def run_candidate(args) -> int:
     to_dev = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
     names = [dlp.proj_candidate_name(w.M, w.N, w.K, w.epi, w.out_dtype, i)
              for i in range(dlp.proj_num_candidates(w.M, w.N, w.K, w.epi, w.out_dtype))]
-    hits = [i for i, n in enumerate(names) if args.candidate in n]
+    hits = [i for i, n in enumerate(names) if n == args.candidate] or \
+        [i for i, n in enumerate(names) if args.candidate in n]
     if not hits:
         print("no candidate contains %r" % args.candidate, file=sys.stderr)
         return 2
@@ -689,11 +761,19 @@ def main() -> int:
                     help="run the first candidate plan whose name contains this text --reps times on the "
                          "workload (for hardware counters; prints only its name and mean time)")
     ap.add_argument("--reps", type=int, default=12, help="runs for --candidate")
+    ap.add_argument("--timeline", default="", metavar="TRACE_CSV",
+                    help="per-call timeline of graph-replayed steps from a rocprofv3 kernel trace CSV")
+    ap.add_argument("--kernels", nargs="+", default=["zero_f32_kernel", "stream_kernel", "splitk_reduce_kernel"],
+                    help="for --timeline: name parts of the kernels of one call, the first one opening a call")
+    ap.add_argument("--gap-us", type=float, default=20.0,
+                    help="for --timeline: largest gap between replayed calls")
     ap.add_argument("--no-workloads", action="store_true",
                     help="time only the headline workload (skip the other four)")
     ap.add_argument("--plans", nargs="+", default=[],
                     help="for --ingest: one-pass stream plans to take counters for")
     args = ap.parse_args()
+    if args.timeline:
+        return timeline(args)
     if args.ingest:
         return ingest_counters(args)
     if args.copy_calibration:
