@@ -309,10 +309,9 @@ std::vector<Candidate> candidates(const Key &k) {
         for (int i = 0; i < kNumGemmVariants; ++i) {
             const GemmVariant &v = kGemmVariants[i];
             if (k.K % v.kmult != 0) continue;
-            // the persistent kernels (families gemmpp64p*, gemmpp64d*) are the
+            // the persistent kernels (families gemmpp64p, -d, -q, -r) are the
             // GEMMs that read a hi/lo pair
-            const bool persistent = std::strncmp(v.family, "gemmpp64", 8) == 0 &&
-                                    (v.family[8] == 'p' || v.family[8] == 'd');
+            const bool persistent = std::strncmp(v.family, "gemmpp64", 8) == 0 && v.family[8] != '\0';
             if (k.hilo && (!persistent || (k.K / 2) % 64 != 0 || k.K < 128)) continue;
             if (v.kmax > 0 && k.K > v.kmax) continue;
             out.push_back({KIND_GEMM, i, 1, gemm_name(v, 1)});
