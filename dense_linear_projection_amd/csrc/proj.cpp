@@ -309,7 +309,7 @@ std::vector<Candidate> candidates(const Key &k) {
         for (int i = 0; i < kNumGemmVariants; ++i) {
             const GemmVariant &v = kGemmVariants[i];
             if (k.K % v.kmult != 0) continue;
-            // the persistent kernels (families gemmpp64p, -d, -q, -r) are the
+            // the persistent kernels (families gemmpp64p and gemmpp64d) are the
             // GEMMs that read a hi/lo pair
             const bool persistent = std::strncmp(v.family, "gemmpp64", 8) == 0 && v.family[8] != '\0';
             if (k.hilo && (!persistent || (k.K / 2) % 64 != 0 || k.K < 128)) continue;

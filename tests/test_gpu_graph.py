@@ -131,3 +131,39 @@ def test_tune_refused_under_capture_then_replaces_default(ctx):
     torch.cuda.synchronize()
     assert "tuned" in dlp.proj_get_plan(ctx, M, N, K, dlp.EPI_BIAS, dlp.OUT_F32)
     assert compare.check(host_f64(Y), r)["ok"]
+
+
+def test_atomic_split_plans_replay_fresh_results(ctx):
+    """Plans that zero Y with a kernel and add their split partials into it
+    with atomics, captured in a graph: every replay, with eager work and a
+    new X between replays, gives the oracle's result (no accumulation across
+    replays, no memset node whose replays could go stale).  Integer inputs
+    keep every order of the additions exact, so replays are compared bit for
+    bit."""
+    import torch
+    M, N, K = 16, 1024, 8192
+    names = [dlp.proj_candidate_name(M, N, K, dlp.EPI_BIAS, dlp.OUT_F32, i)
+             for i in range(dlp.proj_num_candidates(M, N, K, dlp.EPI_BIAS, dlp.OUT_F32))]
+    atomic = [(i, n) for i, n in enumerate(names) if n.endswith("_atomic")]
+    assert atomic
+    W = synth.integer_bf16((N, K), -4, 4, 80)
+    b = synth.integer_bf16((N,), -16, 16, 81)
+    Wd, bd = dev_bf16(W), dev_bf16(b)
+    Xd = dev_bf16(synth.integer_bf16((M, K), -4, 4, 82))
+    Y = out_tensor(M, N, oracle.OUT_F32)
+    s = torch.cuda.Stream()
+    for i, name in atomic[::7] + atomic[-1:]:
+        print("atomic plan in a graph:", name, flush=True)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            dlp.proj_run_candidate(ctx, i, Xd, Wd, bd, dlp.EPI_BIAS, Y, stream=s)
+        for rep in range(4):
+            X = synth.integer_bf16((M, K), -4, 4, 90 + rep)
+            Xd.copy_(dev_bf16(X))
+            Y.fill_(float(rep + 1))              # eager work between replays
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            r, _ = oracle.reference(X, W, b, oracle.EPI_BIAS, oracle.OUT_F32)
+            assert np.array_equal(host_f64(Y), r), (name, rep)
+        del g
