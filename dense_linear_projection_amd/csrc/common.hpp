@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace proj {
@@ -15,20 +16,24 @@ typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 enum Epi { EPI_NONE = 0, EPI_BIAS = 1, EPI_GELU = 2, EPI_BIAS_GELU = 3 };
 enum Out { OUT_F32 = 0, OUT_BF16 = 1 };
 
-// Everything a kernel needs to know about one call.
+// Everything a kernel needs to know about one call.  The fields a kernel
+// reads before its first copy come first, so that they share the first
+// 64 bytes of the argument block (one scalar load at kernel entry); the
+// output side follows.
 struct Args {
     const uint16_t *X;     // bf16 [M, K]
     const uint16_t *W;     // bf16 [N, K]
-    const uint16_t *bias;  // bf16 [N] or nullptr
-    void *Y;               // fp32 / bf16 [M, N]
     int64_t M, N, K;
     int64_t kx;            // X row length: K, or K/2 for a hi/lo weight pair (X column k' reads k' mod kx)
     int epi, out;
     int wpack = 0;         // 0: W row-major [N][K]; t > 0: W packed in tiles of 16t rows (see proj_pack_weights)
     int atomic = 0;        // split K (S > 1), fp32 Y: partials are added into Y (zeroed first) with fp32 atomics
+    const uint16_t *bias;  // bf16 [N] or nullptr
+    void *Y;               // fp32 / bf16 [M, N]
     float *ws;             // split-K partials [S][M][N] (library-owned)
     const uint16_t *zeros; // >= 64 zero bytes in device memory, for masked loads
 };
+static_assert(offsetof(Args, atomic) + sizeof(int) == 64, "the prologue's fields fill the first 64 bytes");
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);

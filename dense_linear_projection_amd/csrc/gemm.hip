@@ -53,6 +53,46 @@ namespace proj {
 // in SQ_LDS_BANK_CONFLICT).
 __device__ __forceinline__ int swz128(int row) { return (row >> 1) & 7; }
 
+// Origin of the L-th tile of a BM x BN tiling walked in groups of GM tile
+// rows (tiles_m x tiles_n tiles), so the workgroups that run together share
+// operand blocks.  32-bit arithmetic (the launchers keep the tile count
+// below 2^31) with one division by a runtime value: this runs before a
+// workgroup's first copy, and a 64-bit division by a runtime value is a
+// sequence of over a hundred scalar instructions.
+template <int BM, int BN, int GM>
+__device__ __forceinline__ void group_origin(uint32_t tiles_m, uint32_t tiles_n, uint32_t L, int64_t &m0,
+                                             int64_t &n0) {
+    const uint32_t per_group = GM * tiles_n;
+    const uint32_t g = L / per_group, in = L - g * per_group;
+    const uint32_t first_m = g * GM;
+    const uint32_t gsz = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
+    uint32_t mi, ni;
+    if (gsz == GM) {
+        mi = in % GM;
+        ni = in / GM;
+    } else {
+        ni = in / gsz;
+        mi = in - ni * gsz;
+    }
+    m0 = static_cast<int64_t>(first_m + mi) * BM;
+    n0 = static_cast<int64_t>(ni) * BN;
+}
+
+// Number of a work item after the XCD-contiguous renumbering: dispatch goes
+// round robin over the 8 XCDs (each with its own L2), so items x, x + 8, ...
+// run on one XCD and are given consecutive numbers.
+__device__ __forceinline__ uint32_t xcd_order(uint32_t item, uint32_t count) {
+    return count % 8 == 0 ? (item % 8) * (count / 8) + item / 8 : item;
+}
+
+// Origin of output tile `bid` of a BM x BN tiling of M x N.
+template <int BM, int BN, int GM>
+__device__ __forceinline__ void tile_origin(int64_t M, int64_t N, uint32_t bid, int64_t &m0, int64_t &n0) {
+    const uint32_t tiles_m = static_cast<uint32_t>((M + BM - 1) / BM);
+    const uint32_t tiles_n = static_cast<uint32_t>((N + BN - 1) / BN);
+    group_origin<BM, BN, GM>(tiles_m, tiles_n, xcd_order(bid, tiles_m * tiles_n), m0, n0);
+}
+
 // A workgroup of WM x WN wave64s computes a BM x BN output tile; each wave
 // owns a (BM/WM) x (BN/WN) sub-tile held as 16x16 fp32 accumulators.  LDS
 // row r holds 8 chunks of 8 k; chunk c sits at position c ^ (r & 7).  Two
@@ -75,17 +115,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(Args a) {
     const int64_t M = a.M, N = a.N, K = a.K;
 
     // ---- tile id: XCD-contiguous renumbering, then grouped order
-    const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    const int64_t G = tiles_m * tiles_n;
-    int64_t L = blockIdx.x;
-    if (G % 8 == 0) L = (L % 8) * (G / 8) + L / 8;
-    const int64_t per_group = GM * tiles_n;
-    const int64_t group = L / per_group;
-    const int64_t first_m = group * GM;
-    const int64_t gsz = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
-    const int64_t tm = first_m + (L % per_group) % gsz;
-    const int64_t tn = (L % per_group) / gsz;
-    const int64_t m0 = tm * BM, n0 = tn * BN;
+    int64_t m0, n0;
+    tile_origin<BM, BN, GM>(M, N, blockIdx.x, m0, n0);
 
     // ---- per-lane DMA source rows for this wave's share of the blocks
     // block b covers rows 8b..8b+7; lane l fills row r = 8b + l/8, position
@@ -284,17 +315,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int wm = wave >> 1, wn = wave & 1;
     const int64_t M = a.M, N = a.N, K = a.K;
 
-    const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    const int64_t G = tiles_m * tiles_n;
-    int64_t L = blockIdx.x;
-    if (G % 8 == 0) L = (L % 8) * (G / 8) + L / 8;
-    const int64_t per_group = GM * tiles_n;
-    const int64_t group = L / per_group;
-    const int64_t first_m = group * GM;
-    const int64_t gsz = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
-    const int64_t tm = first_m + (L % per_group) % gsz;
-    const int64_t tn = (L % per_group) / gsz;
-    const int64_t m0 = tm * BM, n0 = tn * BN;
+    int64_t m0, n0;
+    tile_origin<BM, BN, GM>(M, N, blockIdx.x, m0, n0);
 
     // DMA: copy j of a wave is 1 KB block wave + 8 j of the stage (blocks
     // 0..15 hold X rows, the rest W rows); lane l fills row 16b + l/4,
@@ -487,17 +509,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int wm = wave >> 1, wn = wave & 1;
     const int64_t M = a.M, N = a.N, K = a.K;
 
-    const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    const int64_t G = tiles_m * tiles_n;
-    int64_t L = blockIdx.x;
-    if (G % 8 == 0) L = (L % 8) * (G / 8) + L / 8;
-    const int64_t per_group = GM * tiles_n;
-    const int64_t group = L / per_group;
-    const int64_t first_m = group * GM;
-    const int64_t gsz = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
-    const int64_t tm = first_m + (L % per_group) % gsz;
-    const int64_t tn = (L % per_group) / gsz;
-    const int64_t m0 = tm * BM, n0 = tn * BN;
+    int64_t m0, n0;
+    tile_origin<BM, BN, GM>(M, N, blockIdx.x, m0, n0);
 
     // copies: a group's half of an operand half is blocks
     // grp * (BLK/2) + wg + 4 j; lane l of a copy fills row r = 8b + l/8,
@@ -832,45 +845,56 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int grp = wave >> 2, wg = wave & 3;
     const int wm = wave >> 1, wn = wave & 1;
     const int64_t M = a.M, N = a.N, K = a.K;
-    const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    const int64_t G = tiles_m * tiles_n;
-    const int KH = static_cast<int>(K / 64);
+    // Work items are decoded in 32-bit arithmetic (the launcher keeps
+    // tiles x S below 2^31), with one division by a runtime value per item
+    // for S = 1: the decoding runs at the start of every tile, on the path
+    // to its first copies, and a 64-bit division by a runtime value is a
+    // sequence of over a hundred scalar instructions.
+    const uint32_t tiles_m = static_cast<uint32_t>((M + BM - 1) / BM);
+    const uint32_t tiles_n = static_cast<uint32_t>((N + BN - 1) / BN);
+    const uint32_t us = static_cast<uint32_t>(S);
     // work items: (tile, K split) pairs, item = tile * S + split; a split
     // covers k-ranges [KH * split / S, KH * (split + 1) / S), at least two
-    const int64_t GS = G * S;
-    auto krange = [&](int64_t item, int &kb, int &ke) {
-        const int sp = static_cast<int>(item % S);
-        kb = static_cast<int>((static_cast<int64_t>(KH) * sp) / S);
-        ke = static_cast<int>((static_cast<int64_t>(KH) * (sp + 1)) / S);
+    const uint32_t GS = tiles_m * tiles_n * us;
+    const uint32_t KH = static_cast<uint32_t>(K / 64);
+    struct Work {
+        int64_t m0, n0;
+        int kb, ke, split;
     };
-    // item -> tile origin: XCD-contiguous renumbering of the items (a
-    // workgroup's items all lie on its XCD, since gridDim.x is a multiple of
-    // 8), then GM-row groups of tiles
-    auto remap = [&](int64_t item) { return GS % 8 == 0 ? (item % 8) * (GS / 8) + item / 8 : item; };
-    auto origin = [&](int64_t item, int64_t &m0, int64_t &n0) {
-        const int64_t L = remap(item) / S;
-        const int64_t per_group = GM * tiles_n;
-        const int64_t first_m = (L / per_group) * GM;
-        const int64_t gsz = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
-        m0 = (first_m + (L % per_group) % gsz) * BM;
-        n0 = ((L % per_group) / gsz) * BN;
+    // item -> tile origin and k-ranges: XCD-contiguous renumbering of the
+    // items (a workgroup's items all lie on its XCD, since gridDim.x is a
+    // multiple of 8), then GM-row groups of tiles
+    auto decode = [&](uint32_t item) -> Work {
+        const uint32_t r = xcd_order(item, GS);
+        Work w;
+        uint32_t L = r;
+        w.split = 0;
+        w.kb = 0;
+        w.ke = static_cast<int>(KH);
+        if (us > 1) {
+            L = r / us;
+            const uint32_t sp = r - L * us;
+            w.split = static_cast<int>(sp);
+            w.kb = static_cast<int>((KH * sp) / us);
+            w.ke = static_cast<int>((KH * (sp + 1)) / us);
+        }
+        group_origin<BM, BN, GM>(tiles_m, tiles_n, L, w.m0, w.n0);
+        return w;
     };
     // buffer resources over an item's tile's valid X and W rows, and the
     // item's first k-range (empty resources past the last item)
-    auto resources = [&](int64_t item, __amdgpu_buffer_rsrc_t &ra, __amdgpu_buffer_rsrc_t &rb, int &kb) {
+    auto resources = [&](uint32_t item, __amdgpu_buffer_rsrc_t &ra, __amdgpu_buffer_rsrc_t &rb, int &kb) {
         if (item >= GS) {
             ra = rb = buffer_rsrc(a.X, 0);
             kb = 0;
             return;
         }
-        int ke;
-        krange(remap(item), kb, ke);
-        int64_t m0, n0;
-        origin(item, m0, n0);
-        const int64_t rows_a = (M - m0) < BM ? (M - m0) : BM;
-        const int64_t rows_b = (N - n0) < BN ? (N - n0) : BN;
-        ra = buffer_rsrc(a.X + m0 * a.kx, static_cast<uint32_t>(rows_a * a.kx * 2));
-        rb = buffer_rsrc(a.W + n0 * K, static_cast<uint32_t>(rows_b * K * 2));
+        const Work w = decode(item);
+        kb = w.kb;
+        const int64_t rows_a = (M - w.m0) < BM ? (M - w.m0) : BM;
+        const int64_t rows_b = (N - w.n0) < BN ? (N - w.n0) : BN;
+        ra = buffer_rsrc(a.X + w.m0 * a.kx, static_cast<uint32_t>(rows_a * a.kx * 2));
+        rb = buffer_rsrc(a.W + w.n0 * K, static_cast<uint32_t>(rows_b * K * 2));
     };
 
     const int drow = lane >> 3;
@@ -913,57 +937,63 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     };
     static_assert(!DIRECT || FN % 2 == 0, "DIRECT takes W blocks in pairs");
 
-    int64_t item = blockIdx.x;
+    uint32_t item = blockIdx.x;
     __amdgpu_buffer_rsrc_t ca, cb, na, nb;
     int ckb, nkb;
     resources(item, ca, cb, ckb);
-    resources(item + gridDim.x, na, nb, nkb);
     // slot of A of the current k-range (half index 2g for the g-th k-range
     // this workgroup handles, counted across items)
     int s0 = 0;
     copy_a(ca, ckb, 0);
     copy_b(cb, ckb, 1);
     copy_a(ca, ckb + 1, 2);
+    // the next item's resources while the first copies are in flight
+    resources(item + gridDim.x, na, nb, nkb);
     wait_vm<NCA>();
     barrier_nofence();
 
     for (; item < GS; item += gridDim.x) {
-        int64_t m0, n0;
-        origin(item, m0, n0);
-        int kb, ke;
-        krange(remap(item), kb, ke);
-        const int split = static_cast<int>(remap(item) % S);
-        // bias of this lane's output features: column j * 16 + fr of block
-        // j, or (DIRECT) features 8 fg .. +7 of pair jp as packed bf16
+        const Work cur = decode(item);
+        const int64_t m0 = cur.m0, n0 = cur.n0;
+        const int kb = cur.kb, ke = cur.ke, split = cur.split;
+        // Bias bits of this lane's output features (column j * 16 + fr of
+        // block j, or (DIRECT) features 8 fg .. +7 of pair jp as packed
+        // bf16), read through a resource over the N bias values: features
+        // past N, and every feature when there is no bias, read zero.  They
+        // are converted only in the epilogue.  Using them here would wait
+        // for these loads, and loads and stores complete in order, so that
+        // wait would also take in every copy and every store of the
+        // previous tile's output still in flight.
         constexpr int NB = DIRECT ? 1 : FN;
         constexpr int NBP = DIRECT ? FN / 2 : 1;
-        float bias[NB];
+        const __amdgpu_buffer_rsrc_t rbias = buffer_rsrc(a.bias, (a.epi & 1) ? static_cast<uint32_t>(N * 2) : 0u);
+        uint16_t braw[NB];
         u32x4 biasp[NBP];
         if constexpr (!DIRECT) {
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
                 const int64_t n = n0 + wn * TN + j * 16 + fr;
-                bias[j] = ((a.epi & 1) && n < N) ? bf16_bits_to_f32(a.bias[n]) : 0.f;
+                braw[j] = __builtin_amdgcn_raw_buffer_load_b16(rbias, static_cast<int>(n * 2), 0, 0);
             }
-        } else {
-            const bool vec = (reinterpret_cast<uintptr_t>(a.bias) % 16) == 0;
+        } else if (N % 8 == 0) {
+            // a lane's 8 features lie wholly inside or wholly past N
 #pragma unroll
             for (int jp = 0; jp < FN / 2; ++jp) {
                 const int64_t n = n0 + wn * TN + jp * 32 + 8 * fg;
-                if (!(a.epi & 1) || n >= N) {
-                    biasp[jp] = u32x4{0u, 0u, 0u, 0u};
-                } else if (vec && n + 8 <= N) {
-                    biasp[jp] = *reinterpret_cast<const u32x4 *>(a.bias + n);
-                } else {
-                    uint32_t w[4];
+                biasp[jp] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rbias, static_cast<int>(n * 2), 0, 0));
+            }
+        } else {
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const uint32_t lo = n + 2 * q < N ? a.bias[n + 2 * q] : 0u;
-                        const uint32_t hi = n + 2 * q + 1 < N ? a.bias[n + 2 * q + 1] : 0u;
-                        w[q] = lo | (hi << 16);
-                    }
-                    biasp[jp] = u32x4{w[0], w[1], w[2], w[3]};
+            for (int jp = 0; jp < FN / 2; ++jp) {
+                const int64_t n = n0 + wn * TN + jp * 32 + 8 * fg;
+                uint32_t w[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(rbias, static_cast<int>((n + 2 * q) * 2), 0, 0);
+                    const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(rbias, static_cast<int>((n + 2 * q + 1) * 2), 0, 0);
+                    w[q] = lo | (hi << 16);
                 }
+                biasp[jp] = u32x4{w[0], w[1], w[2], w[3]};
             }
         }
         f32x4 acc[FM][FN];
@@ -1025,6 +1055,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if constexpr (DIRECT) {
             direct_epilogue<FM, FN>(a, acc, biasp, S, split, m0 + wm * TM, n0 + wn * TN, fr, fg);
         } else {
+        float bias[FN];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bias[j] = bf16_bits_to_f32(braw[j]);
         // ---- epilogue.  The slots of the last k-range's A and B (s0 + 3,
         // s0 + 4) are free once every wave's reads of it have landed; the
         // next tile's A(0), B(0), A(1) are in the other three.
@@ -1100,7 +1133,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
         ca = na;
         cb = nb;
-        resources(item + 2 * static_cast<int64_t>(gridDim.x), na, nb, nkb);
+        resources(item + 2 * gridDim.x, na, nb, nkb);
     }
     // the copies issued for the tile after the last one (empty resource)
     // still write LDS: drain them before the workgroup ends

@@ -97,14 +97,28 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(Args a, int S) {
     __shared__ float red[WAVES * V];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int tile = blockIdx.x / S, split = blockIdx.x % S;
+    // 32-bit arithmetic and no division at all for S = 1: this runs before
+    // the first load is issued (the launcher keeps the chunk count times S
+    // below 2^32 for S > 1)
+    const uint32_t us = static_cast<uint32_t>(S);
+    uint32_t tile_u = blockIdx.x, split_u = 0;
+    if (us > 1) {
+        tile_u = blockIdx.x / us;
+        split_u = blockIdx.x - tile_u * us;
+    }
+    const int split = static_cast<int>(split_u);
     const int64_t N = a.N, K = a.K, M = a.M;
-    const int64_t n0 = static_cast<int64_t>(tile) * R;
+    const int64_t n0 = static_cast<int64_t>(tile_u) * R;
     const int64_t rows_w = (N - n0) < R ? (N - n0) : R;
 
     // chunk range of this split
     const int64_t C = K / 8;
-    const int64_t cb = (C * split) / S, ce = (C * (split + 1)) / S;
+    int64_t cb = 0, ce = C;
+    if (us > 1) {
+        const uint32_t c32 = static_cast<uint32_t>(C);
+        cb = (c32 * split_u) / us;
+        ce = (c32 * (split_u + 1)) / us;
+    }
 
     const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(a.W + n0 * K, static_cast<uint32_t>(rows_w * K * 2));
     const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(a.X, static_cast<uint32_t>(M * a.kx * 2));
@@ -183,6 +197,8 @@ static hipError_t launch_gemv(const Args &a, int S, hipStream_t st) {
     if (static_cast<int64_t>(R) * a.K * 2 > 0x7fffffff || a.M * a.kx * 2 > 0x7fffffff) return hipErrorInvalidValue;
     const int64_t grid = ((a.N + R - 1) / R) * S;
     if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    // the kernel cuts the chunk range of a split in 32-bit arithmetic
+    if (S > 1 && (a.K / 8) * S >= (int64_t{1} << 32)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((gemv_kernel<MR, R, WV, U, WNT>), dim3(static_cast<unsigned>(grid)), dim3(WV * 64), 0, st, a,
                        S);
     hipError_t e = hipGetLastError();

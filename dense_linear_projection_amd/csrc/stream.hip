@@ -110,21 +110,41 @@ __global__ __launch_bounds__(WAVES * 64) void stream_kernel(Args a, int S) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t K = a.K, N = a.N;
-    // the launcher keeps the grid (row blocks x tiles x S) below 2^31
-    const uint32_t tS = static_cast<uint32_t>((N + C::NR - 1) / C::NR) * static_cast<uint32_t>(S);
-    const int64_t mb = blockIdx.x / tS;
-    const int tile = static_cast<int>((blockIdx.x % tS) / static_cast<uint32_t>(S)), split = blockIdx.x % S;
+    // Workgroup coordinates in 32-bit arithmetic, with no division at all
+    // for one row block and S = 1: this runs before the first copy is
+    // issued, and a 64-bit division by a runtime value is a sequence of
+    // over a hundred scalar instructions.  The launcher keeps the grid
+    // (row blocks x tiles x S) below 2^31 and, for S > 1, the stage count
+    // times S below 2^32.
+    const uint32_t us = static_cast<uint32_t>(S);
+    uint32_t mbu = 0, rest = blockIdx.x;
+    if (a.M > C::MR) {
+        const uint32_t tS = static_cast<uint32_t>((N + C::NR - 1) / C::NR) * us;
+        mbu = rest / tS;
+        rest -= mbu * tS;
+    }
+    uint32_t tile_u = rest, split_u = 0;
+    if (us > 1) {
+        tile_u = rest / us;
+        split_u = rest - tile_u * us;
+    }
+    const int tile = static_cast<int>(tile_u), split = static_cast<int>(split_u);
     const int64_t n0 = static_cast<int64_t>(tile) * C::NR;
     // this workgroup's token rows: m0 .. m0 + M - 1 (M counted from m0)
-    const int64_t m0 = mb * C::MR;
+    const int64_t m0 = static_cast<int64_t>(mbu) * C::MR;
     const int64_t M = (a.M - m0) < C::MR ? (a.M - m0) : C::MR;
     const uint16_t *X = a.X + m0 * a.kx;
 
     // stage range of this split, and the rotated walk over it
     const int64_t T = (K + KC - 1) / KC;
-    const int64_t sb = (T * split) / S, se = (T * (split + 1)) / S;
+    int64_t sb = 0, se = T;
+    if (us > 1) {
+        const uint32_t t32 = static_cast<uint32_t>(T);
+        sb = (t32 * split_u) / us;
+        se = (t32 * (split_u + 1)) / us;
+    }
     const int nst = static_cast<int>(se - sb);
-    const int rot = nst > 0 ? static_cast<int>((static_cast<int64_t>(tile) * 7) % nst) : 0;
+    const int rot = nst > 0 ? static_cast<int>((tile_u * 7u) % static_cast<uint32_t>(nst)) : 0;
     auto stage_k0 = [&](int i) -> int64_t {
         int q = i + rot;
         if (q >= nst) q -= nst;
@@ -294,8 +314,15 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(Args a, int S) {
     if (idx >= MN) return;
     float s = 0.f;
     for (int sp = 0; sp < S; ++sp) s += a.ws[sp * MN + idx];
-    const int64_t n = idx % a.N;
-    const float b = (a.epi & 1) ? bf16_bits_to_f32(a.bias[n]) : 0.f;
+    float b = 0.f;
+    if (a.epi & 1) {
+        // the bias column; a 32-bit remainder where the output allows (the
+        // 64-bit one is a long instruction sequence per thread)
+        const int64_t n = MN < (int64_t{1} << 32) ? static_cast<int64_t>(static_cast<uint32_t>(idx) %
+                                                                          static_cast<uint32_t>(a.N))
+                                                  : idx % a.N;
+        b = bf16_bits_to_f32(a.bias[n]);
+    }
     store_out(a.Y, a.out, idx, apply_epilogue(s, a.epi, b));
 }
 
@@ -345,6 +372,8 @@ static hipError_t launch_stream(const Args &a, int S, hipStream_t st) {
     const int64_t mblocks = (a.M + 16 * MT - 1) / (16 * MT);
     const int64_t grid = mblocks * tiles * S;
     if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    // the kernel cuts the stage range of a split in 32-bit arithmetic
+    if (S > 1 && ((a.K + KC - 1) / KC) * S >= (int64_t{1} << 32)) return hipErrorInvalidConfiguration;
     constexpr int lds_bytes = StreamCfg<MT, NT, WV, KC, D>::LDS;
     // the buffer-resource path needs whole stages and 32-bit operand offsets;
     // it is also the only one that reads a hi/lo pair's X (kx < K), whose
