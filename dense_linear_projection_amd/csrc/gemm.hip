@@ -740,13 +740,19 @@ __device__ __forceinline__ void direct_epilogue(const Args &a, const f32x4 (&acc
                 const int64_t n = ncol0 + jp * 32 + 8 * fg;
                 if (m >= M || n >= N) continue;
                 float *dst = ws + m * N + n;
+                // plus the bias registers, which read zero here (see the
+                // caller): every path reads them
+                float v[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    v[e] = (e < 4 ? acc[i][2 * jp][e] : acc[i][2 * jp + 1][e - 4]) + bf16_at(biasp[jp], e);
                 if (vec && n + 8 <= N) {
-                    __builtin_nontemporal_store(acc[i][2 * jp], reinterpret_cast<f32x4 *>(dst));
-                    __builtin_nontemporal_store(acc[i][2 * jp + 1], reinterpret_cast<f32x4 *>(dst + 4));
+                    __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4 *>(dst));
+                    __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]}, reinterpret_cast<f32x4 *>(dst + 4));
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
-                        if (n + e < N) dst[e] = e < 4 ? acc[i][2 * jp][e] : acc[i][2 * jp + 1][e - 4];
+                        if (n + e < N) dst[e] = v[e];
                 }
             }
         }
@@ -760,12 +766,15 @@ __device__ __forceinline__ void direct_epilogue(const Args &a, const f32x4 (&acc
         for (int jp = 0; jp < FN / 2; ++jp) {
             const int64_t n = ncol0 + jp * 32 + 8 * fg;
             if (m >= M || n >= N) continue;
+            // the bias is added even when there is none (it reads zero
+            // then): a sum started at +0 is never -0, so adding +0 changes
+            // nothing, and the bias registers are then read on every path
+            // (a loaded register left unread stays pending into the next
+            // tile, whose first reuse of it would wait behind the stores)
             float v[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                v[e] = e < 4 ? acc[i][2 * jp][e] : acc[i][2 * jp + 1][e - 4];
-                if (a.epi & 1) v[e] += bf16_at(biasp[jp], e);
-            }
+            for (int e = 0; e < 8; ++e)
+                v[e] = (e < 4 ? acc[i][2 * jp][e] : acc[i][2 * jp + 1][e - 4]) + bf16_at(biasp[jp], e);
             if (a.epi & 2) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) v[e] = gelu_tanh_fast(v[e]);
@@ -963,10 +972,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // are converted only in the epilogue.  Using them here would wait
         // for these loads, and loads and stores complete in order, so that
         // wait would also take in every copy and every store of the
-        // previous tile's output still in flight.
+        // previous tile's output still in flight.  The loads are issued on
+        // every path and every epilogue path adds what they read (zero
+        // when there is no bias, and for a K split, S > 1, whose bias the
+        // reduction adds): a loaded register left unread is still pending
+        // when the next tile reuses it, and that reuse would wait the same
+        // way.  A sum started at +0 is never -0, so adding +0 changes
+        // nothing.
         constexpr int NB = DIRECT ? 1 : FN;
         constexpr int NBP = DIRECT ? FN / 2 : 1;
-        const __amdgpu_buffer_rsrc_t rbias = buffer_rsrc(a.bias, (a.epi & 1) ? static_cast<uint32_t>(N * 2) : 0u);
+        const __amdgpu_buffer_rsrc_t rbias =
+            buffer_rsrc(a.bias, ((a.epi & 1) && S == 1) ? static_cast<uint32_t>(N * 2) : 0u);
         uint16_t braw[NB];
         u32x4 biasp[NBP];
         if constexpr (!DIRECT) {
@@ -1076,7 +1092,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
                         const int64_t m = m0 + wm * TM + i * 16 + 4 * fg + v;
-                        if (m < M) __builtin_nontemporal_store(acc[i][j][v], ws + m * N + n);
+                        if (m < M) __builtin_nontemporal_store(acc[i][j][v] + bias[j], ws + m * N + n);
                     }
             }
         } else if (full) {

@@ -43,7 +43,8 @@
 //     I avoid reading all those router partials back?"); the order of the
 //     additions then varies from run to run, so the result is correct within
 //     rounding, not bit-reproducible, unless every sum is exact;
-//   * workgroups walk their stages starting at a tile-dependent rotation, so
+//   * workgroups walk their stages starting at a tile-dependent rotation
+//     (tile times the golden ratio, modulo 1, scaled to the stage count), so
 //     at any moment the machine's reads are spread over all of K rather than
 //     all hitting the same column offset of every power-of-two-strided row.
 // Chunks past K or rows past M / N read the zero page (no load leaves the
@@ -144,7 +145,10 @@ __global__ __launch_bounds__(WAVES * 64) void stream_kernel(Args a, int S) {
         se = (t32 * (split_u + 1)) / us;
     }
     const int nst = static_cast<int>(se - sb);
-    const int rot = nst > 0 ? static_cast<int>((tile_u * 7u) % static_cast<uint32_t>(nst)) : 0;
+    // start of the walk: the fractional part of tile * (golden ratio)
+    // scaled to the stage count (a multiply-high, no division), so
+    // neighbouring tiles start far apart in K
+    const int rot = static_cast<int>(__umulhi(tile_u * 0x9E3779B9u, static_cast<uint32_t>(nst > 0 ? nst : 0)));
     auto stage_k0 = [&](int i) -> int64_t {
         int q = i + rot;
         if (q >= nst) q -= nst;
@@ -185,8 +189,12 @@ __global__ __launch_bounds__(WAVES * 64) void stream_kernel(Args a, int S) {
             const int chunk = (lane % C::CPR) ^ (row & 15);
             // W rows are K long (packed: chunk c of a row sits in 128-column
             // block c / 16 of the stage), X rows kx long
-            const int64_t wofs = packed ? (chunk / 16) * C::NR * 128 + row * 128 + (chunk % 16) * 8 : row * K + chunk * 8;
-            voff[j] = static_cast<uint32_t>(row < C::NR ? wofs * 2 : ((row - C::NR) * a.kx + chunk * 8) * 2);
+            // 32-bit: the tile's W rows and the X rows span less than 4 GiB
+            // on this path
+            const uint32_t wofs = packed ? (chunk / 16) * C::NR * 128 + row * 128 + (chunk % 16) * 8
+                                         : static_cast<uint32_t>(row) * static_cast<uint32_t>(K) + chunk * 8;
+            voff[j] = row < C::NR ? wofs * 2
+                                  : (static_cast<uint32_t>(row - C::NR) * static_cast<uint32_t>(a.kx) + chunk * 8) * 2;
         }
     }
     auto issue = [&](int i) {
