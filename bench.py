@@ -189,14 +189,26 @@ def timeline(args) -> int:
     back to back (a call follows the previous one within --gap-us).  The
     calls are the dispatches of kernels whose name contains one of
     --kernels, grouped so that each group starts with the first of those
-    names."""
+    names.  The same kernel may also run for other workloads in the same
+    process: --grid NAME_PART:WORK_ITEMS keeps, of the kernels whose name
+    contains NAME_PART, only the dispatches of that grid size, and
+    --near-us keeps only calls whose kernels span within a factor of 2 of
+    that many microseconds."""
     import csv
+    grids = []
+    for g in args.grid:
+        part, items = g.rsplit(":", 1)
+        grids.append((part, int(items)))
     rows = []
     with open(args.timeline) as f:
         for r in csv.DictReader(f):
             name = r["Kernel_Name"]
-            if any(k in name for k in args.kernels):
-                rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), name))
+            if not any(k in name for k in args.kernels):
+                continue
+            size = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            if any(part in name and size != items for part, items in grids):
+                continue
+            rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), name))
     rows.sort()
     first = args.kernels[0]
     calls, cur = [], []
@@ -207,12 +219,17 @@ def timeline(args) -> int:
         cur.append(r)
     if cur:
         calls.append(cur)
-    shape = [len(c) for c in calls]
-    n = max(set(shape), key=shape.count) if shape else 0
+    # a call launches each of --kernels once
+    n = len(args.kernels)
     steady = []
     for i in range(1, len(calls) - 1):
         c, nxt, prev = calls[i], calls[i + 1], calls[i - 1]
         if len(c) != n or (c[0][0] - prev[-1][1]) > args.gap_us * 1e3 or (nxt[0][0] - c[-1][1]) > args.gap_us * 1e3:
+            continue
+        # --near-us: only calls whose kernels span within a factor of 2 of
+        # it (other workloads' calls of the same kernel and grid differ)
+        span = (c[-1][1] - c[0][0]) / 1e3
+        if args.near_us > 0 and not (args.near_us / 2 <= span <= 2 * args.near_us):
             continue
         steady.append((c, nxt[0][0]))
     if not steady:
@@ -767,6 +784,10 @@ def main() -> int:
                     help="for --timeline: name parts of the kernels of one call, the first one opening a call")
     ap.add_argument("--gap-us", type=float, default=20.0,
                     help="for --timeline: largest gap between replayed calls")
+    ap.add_argument("--grid", nargs="*", default=[], metavar="NAME_PART:WORK_ITEMS",
+                    help="for --timeline: keep only dispatches of that grid size for kernels whose name has NAME_PART")
+    ap.add_argument("--near-us", type=float, default=0.0,
+                    help="for --timeline: keep only calls whose kernels span within a factor of 2 of this")
     ap.add_argument("--no-workloads", action="store_true",
                     help="time only the headline workload (skip the other four)")
     ap.add_argument("--plans", nargs="+", default=[],
