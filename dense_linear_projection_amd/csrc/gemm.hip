@@ -983,7 +983,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         constexpr int NBP = DIRECT ? FN / 2 : 1;
         const __amdgpu_buffer_rsrc_t rbias =
             buffer_rsrc(a.bias, ((a.epi & 1) && S == 1) ? static_cast<uint32_t>(N * 2) : 0u);
-        uint16_t braw[NB];
+        uint32_t braw[NB];  // one 32-bit register each: packing two would wait for both loads
         u32x4 biasp[NBP];
         if constexpr (!DIRECT) {
 #pragma unroll
@@ -1073,7 +1073,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         } else {
         float bias[FN];
 #pragma unroll
-        for (int j = 0; j < FN; ++j) bias[j] = bf16_bits_to_f32(braw[j]);
+        for (int j = 0; j < FN; ++j) {
+            // the empty asm keeps the conversion (and the compiler's wait for
+            // the load) here rather than hoisted up to the load
+            uint32_t bits = braw[j];
+            asm volatile("" : "+v"(bits));
+            bias[j] = bf16_bits_to_f32(bits);
+        }
         // ---- epilogue.  The slots of the last k-range's A and B (s0 + 3,
         // s0 + 4) are free once every wave's reads of it have landed; the
         // next tile's A(0), B(0), A(1) are in the other three.

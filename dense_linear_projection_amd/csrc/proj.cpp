@@ -15,6 +15,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -611,28 +612,40 @@ proj_status tune(proj_ctx *c, const Key &k, const Args &a, hipStream_t st, Plan 
     // and thermal drift over the tuning run falls on all of them alike.
     // Where P >= 2 copies of the operands fill at least half the flush
     // buffer (more than the last-level cache), each leader is timed as a
-    // model replays it: a HIP graph of P calls cycling over the copies, so
+    // model replays it: a HIP graph of calls cycling over the copies, so
     // every call reads its operands from HBM and back-to-back kernels
-    // (split-K passes, zero fills) run with graph launch gaps.  Single cold
-    // launches carry a launch overhead of their own that reorders plans of a
-    // few microseconds.  Otherwise the leaders are timed as in pass 1.
+    // (split-K passes, zero fills) run with graph launch gaps.  The graph
+    // holds about 400 us of calls (a whole number of cycles, at most 256
+    // calls), so the launch and event overhead of one measurement, which
+    // varies by a few microseconds, is spread over many calls: with one
+    // cycle of 3 calls it reordered plans 7% apart.  Single cold launches
+    // carry a launch overhead of their own that reorders plans of a few
+    // microseconds.  Otherwise the leaders are timed as in pass 1.
     std::sort(ranked.begin(), ranked.end());
-    auto up256 = [](size_t x) { return (x + 255) / 256 * 256; };
+    // each copy starts on a 2 MiB boundary, as a large allocation does: where
+    // W's rows fall across the memory channels changes which ring depth wins
+    auto up2m = [](size_t x) { return (x + (size_t{2} << 20) - 1) / (size_t{2} << 20) * (size_t{2} << 20); };
     const size_t xb = static_cast<size_t>(a.M) * static_cast<size_t>(a.kx) * 2;
     const size_t wb = a.wpack ? static_cast<size_t>(proj_packed_bytes(a.N, a.K, a.wpack))
                               : static_cast<size_t>(a.N) * static_cast<size_t>(a.K) * 2;
     const size_t bb = (a.epi & 1) ? static_cast<size_t>(a.N) * 2 : 0;
-    const size_t set = up256(xb) + up256(wb) + up256(bb);
+    const size_t set = up2m(xb) + up2m(wb) + up2m(bb);
     const size_t P = (fbuf && st && set > 0) ? std::min<size_t>(256, kFlushBytes / set) : 0;
     const bool graphs = P >= 2 && P * set >= kFlushBytes / 2;
     const size_t lead = std::min(ranked.size(), graphs ? size_t{8} : size_t{4});
     std::vector<std::vector<float>> t2(lead);
     bool graphed = false;
+    size_t cycles = 1;
+    if (graphs) {
+        const double per_cycle_us = std::max(1.0, static_cast<double>(ranked[0].first) * static_cast<double>(P));
+        cycles = std::max<size_t>(1, std::min<size_t>(256 / P, static_cast<size_t>(std::ceil(400.0 / per_cycle_us))));
+    }
+    const size_t L = P * cycles;  // calls per graph
     if (graphs) {
         std::vector<Args> sets(P, a);
         bool ok = true;
         for (size_t p = 0; p < P && ok; ++p) {
-            char *x = static_cast<char *>(fbuf) + p * set, *w = x + up256(xb), *b = w + up256(wb);
+            char *x = static_cast<char *>(fbuf) + p * set, *w = x + up2m(xb), *b = w + up2m(wb);
             ok = hipMemcpyAsync(x, a.X, xb, hipMemcpyDeviceToDevice, st) == hipSuccess &&
                  hipMemcpyAsync(w, a.W, wb, hipMemcpyDeviceToDevice, st) == hipSuccess &&
                  (bb == 0 || hipMemcpyAsync(b, a.bias, bb, hipMemcpyDeviceToDevice, st) == hipSuccess);
@@ -647,7 +660,7 @@ proj_status tune(proj_ctx *c, const Key &k, const Args &a, hipStream_t st, Plan 
                 break;
             }
             bool launched = true;
-            for (size_t p = 0; p < P && launched; ++p) launched = launch(cands[ranked[j].second], sets[p], st) == hipSuccess;
+            for (size_t q = 0; q < L && launched; ++q) launched = launch(cands[ranked[j].second], sets[q % P], st) == hipSuccess;
             hipGraph_t gr = nullptr;
             const bool ended = hipStreamEndCapture(st, &gr) == hipSuccess;
             ok = launched && ended && gr && hipGraphInstantiate(&ex[j], gr, nullptr, nullptr, 0) == hipSuccess;
@@ -661,7 +674,7 @@ proj_status tune(proj_ctx *c, const Key &k, const Args &a, hipStream_t st, Plan 
                 ok = hipEventRecord(e0, st) == hipSuccess && hipGraphLaunch(ex[j], st) == hipSuccess &&
                      hipEventRecord(e1, st) == hipSuccess && hipEventSynchronize(e1) == hipSuccess &&
                      hipEventElapsedTime(&ms, e0, e1) == hipSuccess;
-                if (ok) t2[j].push_back(ms * 1000.f / static_cast<float>(P));
+                if (ok) t2[j].push_back(ms * 1000.f / static_cast<float>(L));
             }
         for (hipGraphExec_t x : ex)
             if (x) hipGraphExecDestroy(x);

@@ -239,6 +239,30 @@ __global__ __launch_bounds__(WAVES * 64) void stream_kernel(Args a, int S) {
         for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int fr = lane & 15, fg = lane >> 4;
+    // Bias bits of the outputs this thread finishes in the epilogue (S = 1;
+    // split 0 of an atomic split adds the bias in the epilogue as before),
+    // loaded now, just ahead of the first copies, and converted only there:
+    // the load latency then overlaps the stream instead of following it.
+    // Issued behind the copies they would add to the first stage waits
+    // (loads and stores complete in order), which measured 0.2 us later.
+    // Features past N read zero through the resource bounds.  Only tiles
+    // of at most 4 outputs per thread prefetch (the M = 16 decode tiles);
+    // with more, the compiler's handling of the loaded values (a
+    // zero-extension per value) waits for them right away.
+    constexpr int E = MT * NT * 256;
+    constexpr int QN = (E + WAVES * 64 - 1) / (WAVES * 64);
+    constexpr bool PREFETCH = QN <= 4;
+    uint32_t braw[QN];  // one 32-bit register each: packing two would wait for both loads
+    if (PREFETCH && S == 1 && (a.epi & 1)) {
+        const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(a.bias, (a.epi & 1) ? static_cast<uint32_t>(N * 2) : 0u);
+#pragma unroll
+        for (int q = 0; q < QN; ++q) {
+            const int e = tid + q * WAVES * 64;
+            const int tl = e >> 8, ln = e & 63;
+            const int64_t n = n0 + (tl % NT) * 16 + (ln & 15);
+            braw[q] = __builtin_amdgcn_raw_buffer_load_b16(rb, e < E ? static_cast<int>(n * 2) : -1, 0, 0);
+        }
+    }
 #pragma unroll
     for (int i = 0; i < D - 1; ++i) issue(i);
 
@@ -280,7 +304,6 @@ __global__ __launch_bounds__(WAVES * 64) void stream_kernel(Args a, int S) {
 
     // ---- sum the waves' partial tiles: red[wave][tile][i][lane]
     float *red = reinterpret_cast<float *>(lds);
-    constexpr int E = MT * NT * 256;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -291,7 +314,7 @@ __global__ __launch_bounds__(WAVES * 64) void stream_kernel(Args a, int S) {
 
     const uint16_t *bias = a.bias;
 #pragma unroll
-    for (int q = 0; q < (E + WAVES * 64 - 1) / (WAVES * 64); ++q) {
+    for (int q = 0; q < QN; ++q) {
         const int e = tid + q * WAVES * 64;
         if (e >= E) break;
         float s = 0.f;
@@ -303,7 +326,18 @@ __global__ __launch_bounds__(WAVES * 64) void stream_kernel(Args a, int S) {
         const int64_t n = n0 + (tl % NT) * 16 + (ln & 15);
         if (m >= M || n >= N) continue;
         if (S == 1) {
-            const float b = (a.epi & 1) ? bf16_bits_to_f32(bias[n]) : 0.f;
+            float b = 0.f;
+            if (a.epi & 1) {
+                if constexpr (PREFETCH) {
+                    // the empty asm keeps the conversion (and the compiler's
+                    // wait for the load) here rather than hoisted up to it
+                    uint32_t bits = braw[q];
+                    asm volatile("" : "+v"(bits));
+                    b = bf16_bits_to_f32(bits);
+                } else {
+                    b = bf16_bits_to_f32(bias[n]);
+                }
+            }
             store_out(a.Y, a.out, (m0 + m) * N + n, apply_epilogue(s, a.epi, b));
         } else if (a.atomic) {
             const float b = (split == 0 && (a.epi & 1)) ? bf16_bits_to_f32(bias[n]) : 0.f;
