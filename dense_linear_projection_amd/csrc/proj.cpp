@@ -71,6 +71,7 @@ struct Candidate {
     int splits;   // K ranges over workgroups (1: no split)
     std::string name;
     int atomic = 0;  // splits added into a zeroed fp32 Y with atomics instead of a workspace pass
+    int walk = 0;    // streaming kernel's K-walk start (Args::walk)
 };
 
 struct Plan {
@@ -206,11 +207,22 @@ int mt_for(int64_t M) {
     return need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 0;
 }
 
-std::string stream_name(const StreamVariant &v, int S, bool atomic = false) {
+std::string stream_name(const StreamVariant &v, int S, bool atomic = false, int walk = 0) {
     char b[96];
-    snprintf(b, sizeof b, "stream_mt%d_nt%d_w%d_k%d_d%d%s_s%d%s", v.mt, v.nt, v.waves, v.kc, v.depth,
-             v.wnt ? "_wnt" : "", S, atomic ? "_atomic" : "");
+    snprintf(b, sizeof b, "stream_mt%d_nt%d_w%d_k%d_d%d%s_s%d%s%s", v.mt, v.nt, v.waves, v.kc, v.depth,
+             v.wnt ? "_wnt" : "", S, atomic ? "_atomic" : "", walk ? "_g" : "");
     return b;
+}
+
+// Both K-walk starts of a streaming candidate (stage 7t mod T; golden-ratio
+// hash, suffix _g): which keeps the memory channels busiest depends on the
+// shape and the W layout, so the measurement picks.
+void push_stream(std::vector<Candidate> &out, int i, const StreamVariant &v, int S, int atomic) {
+    for (int walk = 0; walk < 2; ++walk) {
+        Candidate c{KIND_STREAM, i, S, stream_name(v, S, atomic != 0, walk), atomic};
+        c.walk = walk;
+        out.push_back(c);
+    }
 }
 
 // Split partials may be added into Y with fp32 atomics when Y is fp32 and
@@ -255,8 +267,8 @@ std::vector<Candidate> candidates(const Key &k) {
             for (int S : {1, 2, 4, 8, 16}) {
                 if (S > 1 && S > stages) continue;
                 if (mblocks * tiles * S > 0x7fffffff) continue;
-                out.push_back({KIND_STREAM, i, S, stream_name(v, S)});
-                if (S > 1 && atomic_ok(k)) out.push_back({KIND_STREAM, i, S, stream_name(v, S, true), 1});
+                push_stream(out, i, v, S, 0);
+                if (S > 1 && atomic_ok(k)) push_stream(out, i, v, S, 1);
             }
         }
         return out;
@@ -286,8 +298,8 @@ std::vector<Candidate> candidates(const Key &k) {
                 for (int S : {1, 2, 4, 8, 16}) {
                     if (S > 1 && S > stages) continue;
                     if (mblocks * tiles * S > 0x7fffffff) continue;
-                    out.push_back({KIND_STREAM, i, S, stream_name(v, S)});
-                    if (S > 1 && atomic_ok(k)) out.push_back({KIND_STREAM, i, S, stream_name(v, S, true), 1});
+                    push_stream(out, i, v, S, 0);
+                    if (S > 1 && atomic_ok(k)) push_stream(out, i, v, S, 1);
                 }
             }
         }
@@ -389,7 +401,7 @@ Args make_args(proj_ctx *c, const void *X, const void *W, const void *bias, int 
                int64_t K, void *Y, int out, int hilo = 0, int wpack = 0) {
     Args a;
     a.kx = hilo ? K / 2 : K;
-    a.wpack = wpack;
+    a.wpack = static_cast<int16_t>(wpack);
     a.X = static_cast<const uint16_t *>(X);
     a.W = static_cast<const uint16_t *>(W);
     a.bias = static_cast<const uint16_t *>(bias);
@@ -410,6 +422,7 @@ hipError_t launch(const Candidate &cand, const Args &a, hipStream_t st) {
         case KIND_STREAM: {
             Args b = a;
             b.atomic = cand.atomic;
+            b.walk = static_cast<int16_t>(cand.walk);
             return kStreamVariants[cand.variant].launch(b, cand.splits, st);
         }
         case KIND_GEMV: return kGemvVariants[cand.variant].launch(a, cand.splits, st);
@@ -632,7 +645,11 @@ proj_status tune(proj_ctx *c, const Key &k, const Args &a, hipStream_t st, Plan 
     const size_t set = up2m(xb) + up2m(wb) + up2m(bb);
     const size_t P = (fbuf && st && set > 0) ? std::min<size_t>(256, kFlushBytes / set) : 0;
     const bool graphs = P >= 2 && P * set >= kFlushBytes / 2;
-    const size_t lead = std::min(ranked.size(), graphs ? size_t{8} : size_t{4});
+    // 16 leaders where graph timing applies: cold single launches rank some
+    // plan families (workspace splits against atomic splits, the two K-walk
+    // starts of a streaming variant) differently from graph replay, so the
+    // pass-1 top must be wide enough to hold each family's best
+    const size_t lead = std::min(ranked.size(), graphs ? size_t{16} : size_t{4});
     std::vector<std::vector<float>> t2(lead);
     bool graphed = false;
     size_t cycles = 1;

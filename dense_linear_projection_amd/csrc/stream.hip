@@ -44,9 +44,10 @@
 //     additions then varies from run to run, so the result is correct within
 //     rounding, not bit-reproducible, unless every sum is exact;
 //   * workgroups walk their stages starting at a tile-dependent rotation
-//     (tile times the golden ratio, modulo 1, scaled to the stage count), so
-//     at any moment the machine's reads are spread over all of K rather than
-//     all hitting the same column offset of every power-of-two-strided row.
+//     (stage 7t mod T for tile t, or t times the golden ratio modulo 1,
+//     scaled to the stage count; a planner choice, Args::walk), so at any
+//     moment the machine's reads are spread over all of K rather than all
+//     hitting the same column offset of every power-of-two-strided row.
 // Chunks past K or rows past M / N read the zero page (no load leaves the
 // caller's buffers); rows past M / N are not stored.
 //
@@ -145,10 +146,14 @@ __global__ __launch_bounds__(WAVES * 64) void stream_kernel(Args a, int S) {
         se = (t32 * (split_u + 1)) / us;
     }
     const int nst = static_cast<int>(se - sb);
-    // start of the walk: the fractional part of tile * (golden ratio)
-    // scaled to the stage count (a multiply-high, no division), so
-    // neighbouring tiles start far apart in K
-    const int rot = static_cast<int>(__umulhi(tile_u * 0x9E3779B9u, static_cast<uint32_t>(nst > 0 ? nst : 0)));
+    // start of the walk, a planner choice (which one keeps the memory
+    // channels busiest depends on the shape and the W layout): stage 7t mod
+    // T for tile t, or the fractional part of t times the golden ratio,
+    // scaled to the stage count by a multiply-high
+    const uint32_t unst = static_cast<uint32_t>(nst > 0 ? nst : 0);
+    const int rot = nst <= 0 ? 0
+                    : a.walk ? static_cast<int>(__umulhi(tile_u * 0x9E3779B9u, unst))
+                             : static_cast<int>((tile_u * 7u) % unst);
     auto stage_k0 = [&](int i) -> int64_t {
         int q = i + rot;
         if (q >= nst) q -= nst;

@@ -34,8 +34,10 @@ def _inputs(seed=0):
 
 
 def _splits(name):
-    m = re.search(r"_s(\d+)$", name)
-    return int(m.group(1)) if m else 1
+    """Workspace partials of a plan: its K-split count, 1 for plans without a
+    split and for atomic splits (which add into Y and need no workspace)."""
+    m = re.search(r"_s(\d+)(_atomic)?(?:_g)?$", name)
+    return int(m.group(1)) if m and not m.group(2) else 1
 
 
 def _split_candidates():

@@ -91,7 +91,7 @@ def test_power_of_two_scaling_every_variant(ctx):
     X4 = synth.values_to_bf16(oracle.bf16_to_f64(X) * 4.0)
     Wd = dev_bf16(W)
     for i, nm in enumerate(names(M, N, K)):
-        if nm.endswith("_atomic"):
+        if "_atomic" in nm:
             continue
         y1 = run(ctx, i, dev_bf16(X), Wd, M, N, K)
         y4 = run(ctx, i, dev_bf16(X4), Wd, M, N, K)
@@ -124,7 +124,7 @@ def test_repeated_calls_give_fresh_results(ctx):
     for out in (oracle.OUT_BF16, oracle.OUT_F32):
         nms = names(M, N, K, 1, out)
         if out == oracle.OUT_F32:
-            assert any(nm.endswith("_atomic") for nm in nms)
+            assert any("_atomic" in nm for nm in nms)
         for i, nm in enumerate(nms):
             Y = out_tensor(M, N, out)
             for rep in range(3):
