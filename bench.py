@@ -96,7 +96,7 @@ def plan_launch(plan: str, w, cus: int = 256):
     the GEMM kernel, e.g. stream_mt1_nt2_w4_k128_d4_wnt_s1 ->
     ("stream_kernel", "stream_kernel<1, 2, 4, 128, 4, 1, true>", 65536)."""
     import re
-    m = re.fullmatch(r"stream_mt(\d+)_nt(\d+)_w(\d+)_k(\d+)_d(\d+)(_wnt)?_s(\d+)(_atomic)?(_g)?", plan)
+    m = re.fullmatch(r"stream_mt(\d+)_nt(\d+)_w(\d+)_k(\d+)_d(\d+)(_wnt)?_s(\d+)(_atomic)?(_r\d+)?", plan)
     if m is not None:
         mt, nt, waves, kc, d = (int(m.group(i)) for i in range(1, 6))
         wnt, S = m.group(6) is not None, int(m.group(7))

@@ -27,7 +27,7 @@ struct Args {
     int64_t kx;            // X row length: K, or K/2 for a hi/lo weight pair (X column k' reads k' mod kx)
     int epi, out;
     int16_t wpack = 0;     // 0: W row-major [N][K]; t > 0: W packed in tiles of 16t rows (see proj_pack_weights)
-    int16_t walk = 0;      // streaming kernel: where each tile starts its K walk (0: stage 7t mod T, 1: golden-ratio hash of t)
+    int16_t walk = 0;      // streaming kernel: tile t starts its K walk at stage (walk x t) mod T (0: stride 7)
     int atomic = 0;        // split K (S > 1), fp32 Y: partials are added into Y (zeroed first) with fp32 atomics
     const uint16_t *bias;  // bf16 [N] or nullptr
     void *Y;               // fp32 / bf16 [M, N]

@@ -71,7 +71,7 @@ struct Candidate {
     int splits;   // K ranges over workgroups (1: no split)
     std::string name;
     int atomic = 0;  // splits added into a zeroed fp32 Y with atomics instead of a workspace pass
-    int walk = 0;    // streaming kernel's K-walk start (Args::walk)
+    int walk = 0;    // streaming kernel's K-walk stride (Args::walk; 0: 7)
 };
 
 struct Plan {
@@ -209,16 +209,21 @@ int mt_for(int64_t M) {
 
 std::string stream_name(const StreamVariant &v, int S, bool atomic = false, int walk = 0) {
     char b[96];
-    snprintf(b, sizeof b, "stream_mt%d_nt%d_w%d_k%d_d%d%s_s%d%s%s", v.mt, v.nt, v.waves, v.kc, v.depth,
-             v.wnt ? "_wnt" : "", S, atomic ? "_atomic" : "", walk ? "_g" : "");
-    return b;
+    snprintf(b, sizeof b, "stream_mt%d_nt%d_w%d_k%d_d%d%s_s%d%s", v.mt, v.nt, v.waves, v.kc, v.depth,
+             v.wnt ? "_wnt" : "", S, atomic ? "_atomic" : "");
+    std::string n = b;
+    if (walk > 0) n += "_r" + std::to_string(walk);
+    return n;
 }
 
-// Both K-walk starts of a streaming candidate (stage 7t mod T; golden-ratio
-// hash, suffix _g): which keeps the memory channels busiest depends on the
-// shape and the W layout, so the measurement picks.
+// K-walk strides offered for every streaming candidate: tile t starts at
+// stage (stride x t) mod T.  Which one keeps the memory channels busiest
+// depends on the shape and the W layout (stride 7 is best for the
+// M16 N8192 decode shape, stride 1 for the M64 N28672 one, in a sweep of
+// 1, 3, 5, 7, 11, 13, 17, 29 and a golden-ratio hash), so the measurement
+// picks.  Stride 7 carries no suffix, stride 1 is suffixed _r1.
 void push_stream(std::vector<Candidate> &out, int i, const StreamVariant &v, int S, int atomic) {
-    for (int walk = 0; walk < 2; ++walk) {
+    for (int walk : {0, 1}) {
         Candidate c{KIND_STREAM, i, S, stream_name(v, S, atomic != 0, walk), atomic};
         c.walk = walk;
         out.push_back(c);

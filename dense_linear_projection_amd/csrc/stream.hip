@@ -44,10 +44,10 @@
 //     additions then varies from run to run, so the result is correct within
 //     rounding, not bit-reproducible, unless every sum is exact;
 //   * workgroups walk their stages starting at a tile-dependent rotation
-//     (stage 7t mod T for tile t, or t times the golden ratio modulo 1,
-//     scaled to the stage count; a planner choice, Args::walk), so at any
-//     moment the machine's reads are spread over all of K rather than all
-//     hitting the same column offset of every power-of-two-strided row.
+//     (stage s t mod T for tile t, the stride s a planner choice:
+//     Args::walk), so at any moment the machine's reads are spread over all
+//     of K rather than all hitting the same column offset of every
+//     power-of-two-strided row.
 // Chunks past K or rows past M / N read the zero page (no load leaves the
 // caller's buffers); rows past M / N are not stored.
 //
@@ -146,14 +146,13 @@ __global__ __launch_bounds__(WAVES * 64) void stream_kernel(Args a, int S) {
         se = (t32 * (split_u + 1)) / us;
     }
     const int nst = static_cast<int>(se - sb);
-    // start of the walk, a planner choice (which one keeps the memory
-    // channels busiest depends on the shape and the W layout): stage 7t mod
-    // T for tile t, or the fractional part of t times the golden ratio,
-    // scaled to the stage count by a multiply-high
-    const uint32_t unst = static_cast<uint32_t>(nst > 0 ? nst : 0);
-    const int rot = nst <= 0 ? 0
-                    : a.walk ? static_cast<int>(__umulhi(tile_u * 0x9E3779B9u, unst))
-                             : static_cast<int>((tile_u * 7u) % unst);
+    // start of the walk: stage (walk stride x tile) mod T, the stride a
+    // planner choice (Args::walk; 0 means 7).  Which stride keeps the memory
+    // channels busiest depends on the shape and the W layout: on one box,
+    // stride 7 ran M16 N8192 at 21.7 us against 26.9 with stride 1, and
+    // stride 1 ran M64 N28672 at 78.5 us against 86.3 with stride 7.
+    const uint32_t stride = a.walk > 0 ? static_cast<uint32_t>(a.walk) : 7u;
+    const int rot = nst > 0 ? static_cast<int>((tile_u * stride) % static_cast<uint32_t>(nst)) : 0;
     auto stage_k0 = [&](int i) -> int64_t {
         int q = i + rot;
         if (q >= nst) q -= nst;

@@ -30,10 +30,10 @@ def test_plan_launch_names_the_dominant_kernel_and_grid():
     assert bench.plan_launch("stream_mt1_nt1_w4_k128_d6_s4_atomic", w0) == \
         ("stream_kernel", "stream_kernel<1, 1, 4, 128, 6, 0, true>", 64 * 4 * 256)
     assert bench.plan_launch("stream_mt1_nt1_w4_k128_d6_s4", w0)[2] == 64 * 4 * 256
-    # the K-walk start (_g) is a runtime argument of the same kernel
-    assert bench.plan_launch("stream_mt1_nt1_w4_k128_d6_s4_atomic_g", w0) == \
+    # the K-walk stride (_r1) is a runtime argument of the same kernel
+    assert bench.plan_launch("stream_mt1_nt1_w4_k128_d6_s4_atomic_r1", w0) == \
         bench.plan_launch("stream_mt1_nt1_w4_k128_d6_s4_atomic", w0)
-    assert bench.plan_launch("stream_mt4_nt7_w4_k128_d3_s1_g", w3) == bench.plan_launch("stream_mt4_nt7_w4_k128_d3_s1", w3)
+    assert bench.plan_launch("stream_mt4_nt7_w4_k128_d3_s1_r1", w3) == bench.plan_launch("stream_mt4_nt7_w4_k128_d3_s1", w3)
     w4 = synth.WORKLOADS[4]         # M4096 N8192: 512 tiles of 256 x 256, one persistent workgroup per CU
     assert bench.plan_launch("gemmpp64p_256x256x64_w4x2_g4", w4) == \
         ("gemm_pp64p_kernel", "gemm_pp64p_kernel<256, 4, false>", 256 * 512)

@@ -36,7 +36,7 @@ def _inputs(seed=0):
 def _splits(name):
     """Workspace partials of a plan: its K-split count, 1 for plans without a
     split and for atomic splits (which add into Y and need no workspace)."""
-    m = re.search(r"_s(\d+)(_atomic)?(?:_g)?$", name)
+    m = re.search(r"_s(\d+)(_atomic)?(?:_r\d+)?$", name)
     return int(m.group(1)) if m and not m.group(2) else 1
 
 

@@ -27,7 +27,7 @@ SCRATCH_BYTES = 2 << 20
 def _splits(plan):
     """Workspace partials of a plan: its K-split count, 1 for plans without a
     split and for atomic splits (which add into Y and need no workspace)."""
-    m = re.search(r"_s(\d+)(_atomic)?(?:_g)?$", plan.split(" ")[0])
+    m = re.search(r"_s(\d+)(_atomic)?(?:_r\d+)?$", plan.split(" ")[0])
     return int(m.group(1)) if m and not m.group(2) else 1
 
 
