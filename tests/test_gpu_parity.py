@@ -165,6 +165,23 @@ def test_token_counts_around_tile_edges(ctx, M):
     assert rep["ok"], rep
 
 
+@pytest.mark.parametrize("M", [2047, 2048, 2049])
+@pytest.mark.parametrize("N,epi,out", [(777, oracle.EPI_BIAS_GELU, oracle.OUT_BF16),
+                                       (3072, oracle.EPI_BIAS, oracle.OUT_F32)],
+                         ids=["N777_gelu_bf16", "N3072_bias_f32"])
+def test_large_token_counts_around_tile_edges(ctx, M, N, epi, out):
+    """Tuned plan (proj_run) on the large-M path at token counts on both sides
+    of a 256-row tile edge, with an odd N (rows of Y not 16-byte aligned, a
+    ragged last column tile) and with whole column tiles."""
+    K = 1024
+    X, W, b = synth.make_inputs(M, N, K, True, 60 + M)
+    r, _ = oracle.reference(X, W, b, epi, out)
+    Y = out_tensor(M, N, out)
+    dlp.proj_run(ctx, dev_bf16(X), dev_bf16(W), dev_bf16(b), epi, Y)
+    rep = compare.check(host_f64(Y), r)
+    assert rep["ok"], (M, N, dlp.proj_get_plan(ctx, M, N, K, epi, out), rep)
+
+
 def test_generic_path_unaligned_and_odd_k(ctx):
     """K % 8 != 0 and a 2-byte-offset X both route to the generic kernel and
     stay within tolerance."""
