@@ -64,3 +64,35 @@ def test_every_candidate_on_random_shape(ctx, case):
     dlp.proj_run(ctx, Xd, Wd, bd if epi & 1 else None, epi, Y)
     rep = compare.check(host_f64(Y), r)
     assert rep["ok"], (case, dlp.proj_get_plan(ctx, M, N, K, epi, out, aligned), rep)
+
+
+def _packed_cases(n=15, seed=20240612):
+    rng = np.random.RandomState(seed)
+    out = []
+    while len(out) < n:
+        regime = len(out) % 3
+        M = int(rng.randint(1, 17)) if regime == 0 else int(rng.randint(17, 65)) if regime == 1 else \
+            int(rng.randint(65, 513))
+        N = int(np.exp(rng.uniform(np.log(3), np.log(2100))))
+        K = 128 * int(rng.randint(1, 17))
+        if M * N * K > 3e8:
+            continue
+        tile16 = int(rng.choice([1, 2, 4, 7]))
+        out.append((M, N, K, tile16, int(rng.randint(0, 4)), int(rng.randint(0, 2))))
+    return out
+
+
+PACKED_CASES = _packed_cases()
+
+
+@pytest.mark.parametrize("case", PACKED_CASES, ids=lambda c: "M%d_N%d_K%d_t%d_e%d_o%d" % c)
+def test_every_packed_candidate_on_random_shape(ctx, case):
+    """The same on weights registered in the packed tile layout."""
+    from tests.test_gpu_packed import run_all_packed
+    M, N, K, tile16, epi, out = case
+    print("random packed shape", case, flush=True)
+    X, W, b = synth.make_inputs(M, N, K, True, 7100 + M + N + K)
+    r, _ = oracle.reference(X, W, b, epi, out)
+    for name, u in run_all_packed(ctx, X, W, b if epi & 1 else None, epi, out, tile16):
+        rep = compare.check(u, r)
+        assert rep["ok"], (case, name, rep)
