@@ -96,3 +96,50 @@ def test_every_packed_candidate_on_random_shape(ctx, case):
     for name, u in run_all_packed(ctx, X, W, b if epi & 1 else None, epi, out, tile16):
         rep = compare.check(u, r)
         assert rep["ok"], (case, name, rep)
+
+
+def _hilo_cases(n=12, seed=20240613):
+    rng = np.random.RandomState(seed)
+    out = []
+    while len(out) < n:
+        regime = len(out) % 3
+        M = int(rng.randint(1, 17)) if regime == 0 else int(rng.randint(17, 257)) if regime == 1 else \
+            int(rng.randint(257, 700))
+        N = int(np.exp(rng.uniform(np.log(3), np.log(1500))))
+        K = 8 * int(np.exp(rng.uniform(np.log(1), np.log(260))))
+        if M * N * K > 2e8:
+            continue
+        out.append((M, N, K, int(rng.randint(0, 4)), int(rng.randint(0, 2))))
+    return out
+
+
+HILO_CASES = _hilo_cases()
+
+
+@pytest.mark.parametrize("case", HILO_CASES, ids=lambda c: "M%d_N%d_K%d_e%d_o%d" % c)
+def test_every_hilo_candidate_on_random_shape(ctx, case):
+    """fp32 weights registered as a bf16 high/low pair: every candidate
+    against the product with the fp32 weights themselves; with fp32 output
+    and no GELU also the router's per-row rule at 0.01%."""
+    from tests.test_gpu_hilo import dev_f32, reference_f32, router_weights
+    M, N, K, epi, out = case
+    print("random hi/lo shape", case, flush=True)
+    X = synth.normal_bf16((M, K), 1.0, 7200 + M)
+    W = router_weights(N, K, 7201 + N + K)
+    b = synth.normal_bf16((N,), float(np.sqrt(0.02)), 7202)
+    bias = b if epi & 1 else None
+    r = reference_f32(X, W, bias, epi, out)
+    Xd, Whl = dev_bf16(X), dlp.proj_prepare_hilo(ctx, dev_f32(W))
+    bd = dev_bf16(b) if bias is not None else None
+    n = dlp.proj_num_candidates_hilo(M, N, K, epi, out)
+    assert n >= 1
+    for i in range(n):
+        name = dlp.proj_candidate_name_hilo(M, N, K, epi, out, i)
+        Y = out_tensor(M, N, out)
+        dlp.proj_run_candidate_hilo(ctx, i, Xd, Whl, bd, epi, Y)
+        u = host_f64(Y)
+        rep = compare.check(u, r)
+        assert rep["ok"], (case, name, rep)
+        if out == oracle.OUT_F32 and not epi & 2:
+            rows = compare.check_rows(u, r, compare.ROUTER_TOL)
+            assert rows["ok"], (case, name, rows)
