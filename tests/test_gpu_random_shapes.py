@@ -66,6 +66,32 @@ def test_every_candidate_on_random_shape(ctx, case):
     assert rep["ok"], (case, dlp.proj_get_plan(ctx, M, N, K, epi, out, aligned), rep)
 
 
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "M%d_N%d_K%d_e%d_o%d_x%d" % c)
+def test_every_candidate_exact_on_random_integer_shape(ctx, case):
+    """The same shapes with integer inputs in [-8, 8] (bias in [-64, 64]):
+    every partial sum is an exact integer below 2^24, so every candidate must
+    equal the oracle bit for bit (GELU left out: it is not exact), which a
+    tolerance would not guarantee for, say, one k-term dropped at large K."""
+    M, N, K, epi, out, off = case
+    epi &= 1
+    print("random integer shape", case, flush=True)
+    X = synth.integer_bf16((M, K), -8, 8, 7300 + M)
+    W = synth.integer_bf16((N, K), -8, 8, 7301 + N)
+    b = synth.integer_bf16((N,), -64, 64, 7302 + K)
+    r, _ = oracle.reference(X, W, b, epi, out)
+    Xd, Wd, bd = dev_bf16(X, offset_elems=off), dev_bf16(W), dev_bf16(b)
+    aligned = off == 0 and K % 8 == 0
+    n = dlp.proj_num_candidates(M, N, K, epi, out, aligned)
+    for i in range(n):
+        name = dlp.proj_candidate_name(M, N, K, epi, out, i, aligned)
+        Y = out_tensor(M, N, out)
+        dlp.proj_run_candidate(ctx, i, Xd, Wd, bd if epi else None, epi, Y)
+        u = host_f64(Y)
+        bad = np.argwhere(u != r)
+        assert bad.size == 0, "%s %s: %d mismatches, first at %s: %r vs %r" % (
+            case, name, len(bad), bad[0], u[tuple(bad[0])], r[tuple(bad[0])])
+
+
 def _packed_cases(n=15, seed=20240612):
     rng = np.random.RandomState(seed)
     out = []
