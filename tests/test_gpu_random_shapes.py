@@ -1,13 +1,9 @@
-"""GPU parity on seeded random shapes: every candidate plan the planner
-offers for a shape (the validity rules, not a hand-picked list) is run
-through the C ABI and compared with the fp64 oracle on every element.
-
-The shapes are drawn once from a fixed seed across the three regimes the
-planner spans (up to 8 token rows, up to 64, up to 512), with N and K from a
-handful to about two thousand, K sometimes not a multiple of 8, X sometimes
-not 16-byte aligned, every epilogue and both output types.  Inputs are
-N(0, 1) X and N(0, 1/K) W, so the bar is |u - r| <= 2e-3 + 2e-2 |r|.
-"""
+"""Seeded random shapes through the tuned entry points (the plan the tuner
+keeps for each shape), against the oracle: token counts from 1 to 600 (the
+GEMV, streaming, row-block and GEMM regimes), ragged N and K (including K not
+a multiple of 8 and pointers off 16-byte alignment, which take the any-shape
+kernel), every epilogue and both output types; then fp32 weights through the
+hi/lo pair and bf16 weights through the packed layout."""
 import numpy as np
 import pytest
 
@@ -19,153 +15,73 @@ from tests.gpu_helpers import dev_bf16, host_f64, out_tensor
 
 pytestmark = pytest.mark.gpu
 
+torch = pytest.importorskip("torch")
 
-def _cases(n=60, seed=20240611):
-    rng = np.random.RandomState(seed)
+
+def _shapes(seed, n):
+    rng = np.random.default_rng(seed)
     out = []
-    while len(out) < n:
-        regime = len(out) % 3
-        M = int(rng.randint(1, 9)) if regime == 0 else int(rng.randint(9, 65)) if regime == 1 else \
-            int(rng.randint(65, 513))
-        N = int(np.exp(rng.uniform(np.log(3), np.log(2100))))
-        K = int(np.exp(rng.uniform(np.log(8), np.log(2100))))
-        if rng.rand() < 0.75:
-            K = max(8, K // 8 * 8)       # the aligned kernels' K rule
-        if M * N * K > 3e8:              # keeps the oracle at a fraction of a second
-            continue
-        epi = int(rng.randint(0, 4))
-        out_t = int(rng.randint(0, 2))
-        off = 1 if rng.rand() < 0.15 else 0
-        out.append((M, N, K, epi, out_t, off))
+    for _ in range(n):
+        M = int(rng.choice([rng.integers(1, 9), rng.integers(9, 65), rng.integers(65, 600)]))
+        N = int(rng.integers(1, 700))
+        K = int(rng.choice([8 * rng.integers(1, 256), rng.integers(1, 300)]))
+        out.append((M, N, K, int(rng.integers(0, 4)), int(rng.integers(0, 2)), bool(rng.random() < 0.2)))
     return out
 
 
-CASES = _cases()
-
-
-@pytest.mark.parametrize("case", CASES, ids=lambda c: "M%d_N%d_K%d_e%d_o%d_x%d" % c)
-def test_every_candidate_on_random_shape(ctx, case):
-    M, N, K, epi, out, off = case
-    print("random shape", case, flush=True)
-    X, W, b = synth.make_inputs(M, N, K, True, 7000 + M + N + K)
-    r, _ = oracle.reference(X, W, b, epi, out)
-    Xd, Wd, bd = dev_bf16(X, offset_elems=off), dev_bf16(W), dev_bf16(b)
-    aligned = off == 0 and K % 8 == 0
-    n = dlp.proj_num_candidates(M, N, K, epi, out, aligned)
-    assert n >= 1
-    for i in range(n):
-        name = dlp.proj_candidate_name(M, N, K, epi, out, i, aligned)
-        Y = out_tensor(M, N, out)
-        dlp.proj_run_candidate(ctx, i, Xd, Wd, bd if epi & 1 else None, epi, Y)
-        rep = compare.check(host_f64(Y), r)
-        assert rep["ok"], (case, name, rep)
-    # and the plan the tuner keeps for it
-    Y = out_tensor(M, N, out)
-    dlp.proj_run(ctx, Xd, Wd, bd if epi & 1 else None, epi, Y)
-    rep = compare.check(host_f64(Y), r)
-    assert rep["ok"], (case, dlp.proj_get_plan(ctx, M, N, K, epi, out, aligned), rep)
-
-
-@pytest.mark.parametrize("case", CASES, ids=lambda c: "M%d_N%d_K%d_e%d_o%d_x%d" % c)
-def test_every_candidate_exact_on_random_integer_shape(ctx, case):
-    """The same shapes with integer inputs in [-8, 8] (bias in [-64, 64]):
-    every partial sum is an exact integer below 2^24, so every candidate must
-    equal the oracle bit for bit (GELU left out: it is not exact), which a
-    tolerance would not guarantee for, say, one k-term dropped at large K."""
-    M, N, K, epi, out, off = case
-    epi &= 1
-    print("random integer shape", case, flush=True)
-    X = synth.integer_bf16((M, K), -8, 8, 7300 + M)
-    W = synth.integer_bf16((N, K), -8, 8, 7301 + N)
-    b = synth.integer_bf16((N,), -64, 64, 7302 + K)
-    r, _ = oracle.reference(X, W, b, epi, out)
-    Xd, Wd, bd = dev_bf16(X, offset_elems=off), dev_bf16(W), dev_bf16(b)
-    aligned = off == 0 and K % 8 == 0
-    n = dlp.proj_num_candidates(M, N, K, epi, out, aligned)
-    for i in range(n):
-        name = dlp.proj_candidate_name(M, N, K, epi, out, i, aligned)
-        Y = out_tensor(M, N, out)
-        dlp.proj_run_candidate(ctx, i, Xd, Wd, bd if epi else None, epi, Y)
-        u = host_f64(Y)
-        bad = np.argwhere(u != r)
-        assert bad.size == 0, "%s %s: %d mismatches, first at %s: %r vs %r" % (
-            case, name, len(bad), bad[0], u[tuple(bad[0])], r[tuple(bad[0])])
-
-
-def _packed_cases(n=15, seed=20240612):
-    rng = np.random.RandomState(seed)
-    out = []
-    while len(out) < n:
-        regime = len(out) % 3
-        M = int(rng.randint(1, 17)) if regime == 0 else int(rng.randint(17, 65)) if regime == 1 else \
-            int(rng.randint(65, 513))
-        N = int(np.exp(rng.uniform(np.log(3), np.log(2100))))
-        K = 128 * int(rng.randint(1, 17))
-        if M * N * K > 3e8:
-            continue
-        tile16 = int(rng.choice([1, 2, 4, 7]))
-        out.append((M, N, K, tile16, int(rng.randint(0, 4)), int(rng.randint(0, 2))))
-    return out
-
-
-PACKED_CASES = _packed_cases()
-
-
-@pytest.mark.parametrize("case", PACKED_CASES, ids=lambda c: "M%d_N%d_K%d_t%d_e%d_o%d" % c)
-def test_every_packed_candidate_on_random_shape(ctx, case):
-    """The same on weights registered in the packed tile layout."""
-    from tests.test_gpu_packed import run_all_packed
-    M, N, K, tile16, epi, out = case
-    print("random packed shape", case, flush=True)
-    X, W, b = synth.make_inputs(M, N, K, True, 7100 + M + N + K)
-    r, _ = oracle.reference(X, W, b, epi, out)
-    for name, u in run_all_packed(ctx, X, W, b if epi & 1 else None, epi, out, tile16):
-        rep = compare.check(u, r)
-        assert rep["ok"], (case, name, rep)
-
-
-def _hilo_cases(n=12, seed=20240613):
-    rng = np.random.RandomState(seed)
-    out = []
-    while len(out) < n:
-        regime = len(out) % 3
-        M = int(rng.randint(1, 17)) if regime == 0 else int(rng.randint(17, 257)) if regime == 1 else \
-            int(rng.randint(257, 700))
-        N = int(np.exp(rng.uniform(np.log(3), np.log(1500))))
-        K = 8 * int(np.exp(rng.uniform(np.log(1), np.log(260))))
-        if M * N * K > 2e8:
-            continue
-        out.append((M, N, K, int(rng.randint(0, 4)), int(rng.randint(0, 2))))
-    return out
-
-
-HILO_CASES = _hilo_cases()
-
-
-@pytest.mark.parametrize("case", HILO_CASES, ids=lambda c: "M%d_N%d_K%d_e%d_o%d" % c)
-def test_every_hilo_candidate_on_random_shape(ctx, case):
-    """fp32 weights registered as a bf16 high/low pair: every candidate
-    against the product with the fp32 weights themselves; with fp32 output
-    and no GELU also the router's per-row rule at 0.01%."""
-    from tests.test_gpu_hilo import dev_f32, reference_f32, router_weights
-    M, N, K, epi, out = case
-    print("random hi/lo shape", case, flush=True)
-    X = synth.normal_bf16((M, K), 1.0, 7200 + M)
-    W = router_weights(N, K, 7201 + N + K)
-    b = synth.normal_bf16((N,), float(np.sqrt(0.02)), 7202)
+@pytest.mark.parametrize("M,N,K,epi,out,misaligned", _shapes(2024, 30),
+                         ids=lambda v: str(v))
+def test_random_shape_tuned_plan(ctx, M, N, K, epi, out, misaligned):
+    print("random shape", M, N, K, epi, out, misaligned, flush=True)
+    X, W, b = synth.make_inputs(M, N, K, True, 40 + M + N)
     bias = b if epi & 1 else None
-    r = reference_f32(X, W, bias, epi, out)
-    Xd, Whl = dev_bf16(X), dlp.proj_prepare_hilo(ctx, dev_f32(W))
+    r, _ = oracle.reference(X, W, bias, epi, out)
+    off = 1 if misaligned else 0    # one bf16 element: 2-byte aligned, not 16
+    Xd, Wd = dev_bf16(X, off), dev_bf16(W, off)
     bd = dev_bf16(b) if bias is not None else None
-    n = dlp.proj_num_candidates_hilo(M, N, K, epi, out)
-    assert n >= 1
-    for i in range(n):
-        name = dlp.proj_candidate_name_hilo(M, N, K, epi, out, i)
-        Y = out_tensor(M, N, out)
-        dlp.proj_run_candidate_hilo(ctx, i, Xd, Whl, bd, epi, Y)
-        u = host_f64(Y)
-        rep = compare.check(u, r)
-        assert rep["ok"], (case, name, rep)
-        if out == oracle.OUT_F32 and not epi & 2:
-            rows = compare.check_rows(u, r, compare.ROUTER_TOL)
-            assert rows["ok"], (case, name, rows)
+    Y = out_tensor(M, N, out)
+    dlp.proj_run(ctx, Xd, Wd, bd, epi, Y)
+    rep = compare.check(host_f64(Y), r)
+    if not rep["ok"]:
+        try:
+            plan = dlp.proj_get_plan(ctx, M, N, K, epi, out, aligned16=not misaligned and K % 8 == 0)
+        except dlp.ProjError as e:
+            plan = str(e)
+        raise AssertionError((plan, rep))
+
+
+def _router_shapes(seed, n):
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(1, 300)), int(rng.integers(1, 400)), int(64 * rng.integers(1, 64))) for _ in range(n)]
+
+
+@pytest.mark.parametrize("M,N,K", _router_shapes(7, 8), ids=lambda v: str(v))
+def test_random_hilo_shape(ctx, M, N, K):
+    print("random hilo", M, N, K, flush=True)
+    X = synth.normal_bf16((M, K), 1.0, 50 + M)
+    W = (np.random.default_rng(51 + N).standard_normal((N, K)) / np.sqrt(K)).astype(np.float32)
+    r = oracle.round_out(oracle.proj_f64_w32(X, W), oracle.OUT_F32).astype(np.float64)
+    Whl = dlp.proj_prepare_hilo(ctx, torch.from_numpy(W).cuda())
+    Y = out_tensor(M, N, oracle.OUT_F32)
+    dlp.proj_run_hilo(ctx, dev_bf16(X), Whl, None, dlp.EPI_NONE, Y)
+    u = host_f64(Y)
+    rows = compare.check_rows(u, r, compare.ROUTER_TOL)
+    assert compare.check(u, r)["ok"] and rows["ok"], rows
+
+
+def _packed_shapes(seed, n):
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(1, 513)), int(rng.integers(1, 600)), int(128 * rng.integers(1, 24)),
+             int(rng.choice([1, 2, 4, 7]))) for _ in range(n)]
+
+
+@pytest.mark.parametrize("M,N,K,tile16", _packed_shapes(11, 8), ids=lambda v: str(v))
+def test_random_packed_shape(ctx, M, N, K, tile16):
+    print("random packed", M, N, K, tile16, flush=True)
+    X, W, b = synth.make_inputs(M, N, K, True, 60 + M)
+    r, _ = oracle.reference(X, W, b, oracle.EPI_BIAS_GELU, oracle.OUT_BF16)
+    Wp = dlp.proj_pack_weights(ctx, dev_bf16(W), tile16)
+    Y = out_tensor(M, N, oracle.OUT_BF16)
+    dlp.proj_run_packed(ctx, dev_bf16(X), Wp, tile16, dev_bf16(b), dlp.EPI_BIAS_GELU_TANH, Y, N)
+    rep = compare.check(host_f64(Y), r)
+    assert rep["ok"], rep
