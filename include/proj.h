@@ -41,7 +41,9 @@
  *
  * Memory the library owns: per context, the split-K workspace (exactly the
  * caller's bound, given to proj_create) and 1.25 KiB of zero page and sink;
- * per tuning call, the flush buffer above.  Nothing else.
+ * per tuning call, the flush buffer above; per GPU, the 2 MiB static array
+ * of split-K partials that proj_run_noalloc uses (part of the library's code
+ * object, held until the process ends).  Nothing else.
  *
  * Errors: every call returns a proj_status; nothing throws across the ABI.
  * Arguments are validated before any HIP call.  HIP failures return
