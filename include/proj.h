@@ -132,7 +132,14 @@ proj_status proj_create(proj_ctx **ctx, int device, size_t max_workspace_bytes);
  * MFMA GEMMs (any M, K a multiple of 32 or 64), and an any-shape kernel;
  * K may be split over workgroups, with a second kernel adding the fp32
  * partials in split order and applying the epilogue (only plans whose
- * partials fit the context's workspace are considered).
+ * partials fit the context's workspace are considered); for fp32 output
+ * without GELU a split may instead add its partials straight into Y with
+ * fp32 atomics after a fill kernel has zeroed Y (plans named "_atomic").
+ * Every plan except those atomic ones gives the same bits on every run;
+ * with an atomic plan the order of the additions, and so the last bits of
+ * the result, may change from run to run (the result stays within the
+ * accuracy of an fp32 sum).  Integer-valued sums below 2^24 are exact in
+ * every plan.
  *
  * Plan choice (kernel family, tile shape, split count): on the first call
  * for a shape key (M, N, K, epilogue, out dtype, alignment) outside stream
