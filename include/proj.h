@@ -135,11 +135,13 @@ proj_status proj_create(proj_ctx **ctx, int device, size_t max_workspace_bytes);
  * partials fit the context's workspace are considered); for fp32 output
  * without GELU a split may instead add its partials straight into Y with
  * fp32 atomics after a fill kernel has zeroed Y (plans named "_atomic").
- * Every plan except those atomic ones gives the same bits on every run;
- * with an atomic plan the order of the additions, and so the last bits of
- * the result, may change from run to run (the result stays within the
- * accuracy of an fp32 sum).  Integer-valued sums below 2^24 are exact in
- * every plan.
+ * Every plan except those atomic ones gives the same bits on every run of
+ * that plan; with an atomic plan the order of the additions, and so the
+ * last bits of the result, may change from run to run (the result stays
+ * within the accuracy of an fp32 sum).  Different plans add in different
+ * orders, so a shape may round differently in another process that tuned
+ * another plan (PROJ_PLAN_FILE pins the plans).  Integer-valued sums below
+ * 2^24 are exact in every plan.
  *
  * Plan choice (kernel family, tile shape, split count): on the first call
  * for a shape key (M, N, K, epilogue, out dtype, alignment) outside stream
