@@ -318,10 +318,10 @@ proj_status proj_run_candidate_hilo(proj_ctx *ctx, int index, const void *X, con
 proj_status proj_read_probe(proj_ctx *ctx, const void *buf, size_t bytes, void *stream);
 
 /* HIP-graph capture of repeated launches (worklog "How I made Muse's GPU
- * projections 1.32x faster in the Open Kernel Challenge", sections on timing
- * the calls as graphs and "Fresh graph replay is a correctness test too": a
- * replay must follow the X it finds, not an answer kept from an earlier
- * run).  Records n_calls proj_run calls, call i using X[i], W[i], bias[i], Y[i]
+ * projections 1.32x faster in the Open Kernel Challenge", sections "How I
+ * checked whether an idea was actually faster", where the calls ran as
+ * graphs, and "Fresh graph replay is a correctness test too": a replay must
+ * follow the X it finds, not an answer kept from an earlier run).  Records n_calls proj_run calls, call i using X[i], W[i], bias[i], Y[i]
  * (bias may be NULL, or bias[i] NULL, when the epilogue has none), all with
  * one shape, into a graph on `stream`, and instantiates it.  The plan for
  * the shape is tuned first (outside capture) unless PROJ_TUNE=0.  Replaying
