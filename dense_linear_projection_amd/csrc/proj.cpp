@@ -559,7 +559,8 @@ constexpr double kSkipFactor = 20.0;
 // buffers; returns the winner.  The last-level cache is flushed before each
 // timed run when the operands could fit in it, so small shapes are timed as
 // they run from HBM: the flush buffer (kFlushBytes) is allocated for the
-// tuning run and freed before returning.
+// tuning run, and exchanged for the operand copies of the graph timing
+// (below, together no more than kFlushBytes), all freed before returning.
 proj_status tune(proj_ctx *c, const Key &k, const Args &a, hipStream_t st, Plan &plan) {
     std::vector<Candidate> cands = candidates_within(k, c->ws_bytes);
     const size_t bytes = static_cast<size_t>(2 * (k.M + k.N) * k.K);
@@ -628,9 +629,10 @@ proj_status tune(proj_ctx *c, const Key &k, const Args &a, hipStream_t st, Plan 
     }
     // pass 2: the leaders again, interleaved round by round so that clock
     // and thermal drift over the tuning run falls on all of them alike.
-    // Where P >= 2 copies of the operands fill at least half the flush
-    // buffer (more than the last-level cache), each leader is timed as a
-    // model replays it: a HIP graph of calls cycling over the copies, so
+    // Where P >= 2 sets of the operands fill at least half of kFlushBytes
+    // (more than the last-level cache), each leader is timed as a model
+    // replays it: a HIP graph of calls cycling over the caller's operands
+    // and P - 1 copies, so
     // every call reads its operands from HBM and back-to-back kernels
     // (split-K passes, zero fills) run with graph launch gaps.  The graph
     // holds about 400 us of calls (a whole number of cycles, at most 256
@@ -640,8 +642,14 @@ proj_status tune(proj_ctx *c, const Key &k, const Args &a, hipStream_t st, Plan 
     // carry a launch overhead of their own that reorders plans of a few
     // microseconds.  Otherwise the leaders are timed as in pass 1.
     std::sort(ranked.begin(), ranked.end());
-    // each copy starts on a 2 MiB boundary, as a large allocation does: where
-    // W's rows fall across the memory channels changes which ring depth wins
+    // Set 0 of the graph is the caller's buffers; the other sets are copies,
+    // each operand in an allocation of its own.  Where W sits in memory
+    // changes which ring depth wins: with the copies carved out of one
+    // 512 MiB allocation on 2 MiB boundaries, the M=16 K=8192 N=8192 decode
+    // plans came out within 1% of each other (22.8-23.8 us), while with
+    // allocations of their own, as a framework's tensors have, the 4-stage
+    // ring led the 256-column 8-wave form by 7% (21.8 against 23.3 us), as in
+    // use.
     auto up2m = [](size_t x) { return (x + (size_t{2} << 20) - 1) / (size_t{2} << 20) * (size_t{2} << 20); };
     const size_t xb = static_cast<size_t>(a.M) * static_cast<size_t>(a.kx) * 2;
     const size_t wb = a.wpack ? static_cast<size_t>(proj_packed_bytes(a.N, a.K, a.wpack))
@@ -663,12 +671,38 @@ proj_status tune(proj_ctx *c, const Key &k, const Args &a, hipStream_t st, Plan 
         cycles = std::max<size_t>(1, std::min<size_t>(256 / P, static_cast<size_t>(std::ceil(400.0 / per_cycle_us))));
     }
     const size_t L = P * cycles;  // calls per graph
+    // copies for the graph sets, freed when tuning returns
+    struct FreeAll {
+        std::vector<void *> p;
+        ~FreeAll() {
+            for (void *q : p) hipFree(q);
+        }
+    } copies;
     if (graphs) {
+        // the flush buffer is not read from here on (a fallback to single
+        // launches then runs without the flush): let it go before the copies
+        // are allocated, so tuning holds at most 512 MiB of either
+        if (hipStreamSynchronize(st) == hipSuccess) {
+            hipFree(fbuf);
+            free_after.p = fbuf = nullptr;
+            sink = nullptr;
+        }
         std::vector<Args> sets(P, a);
         bool ok = true;
-        for (size_t p = 0; p < P && ok; ++p) {
-            char *x = static_cast<char *>(fbuf) + p * set, *w = x + up2m(xb), *b = w + up2m(wb);
-            ok = hipMemcpyAsync(x, a.X, xb, hipMemcpyDeviceToDevice, st) == hipSuccess &&
+        auto alloc = [&](size_t n) -> char * {
+            void *q = nullptr;
+            if (n == 0) return nullptr;
+            if (hipMalloc(&q, n) != hipSuccess) {
+                (void)hipGetLastError();
+                return nullptr;
+            }
+            copies.p.push_back(q);
+            return static_cast<char *>(q);
+        };
+        for (size_t p = 1; p < P && ok; ++p) {
+            char *x = alloc(xb), *w = alloc(wb), *b = alloc(bb);
+            ok = x && w && (bb == 0 || b) &&
+                 hipMemcpyAsync(x, a.X, xb, hipMemcpyDeviceToDevice, st) == hipSuccess &&
                  hipMemcpyAsync(w, a.W, wb, hipMemcpyDeviceToDevice, st) == hipSuccess &&
                  (bb == 0 || hipMemcpyAsync(b, a.bias, bb, hipMemcpyDeviceToDevice, st) == hipSuccess);
             sets[p].X = reinterpret_cast<const uint16_t *>(x);

@@ -34,14 +34,15 @@
  * default stream).  Once a shape's plan is chosen (the first uncaptured call
  * for a shape measures the candidate plans, synchronising the stream; while
  * it times small shapes it holds a 512 MiB buffer that it reads to flush the
- * caches, allocated for that tuning call and freed before it returns; see
- * proj_run), proj_run only enqueues work and returns: it never
+ * caches, then, in its place, copies of the operands for graph timing (at
+ * most 512 MiB), all allocated for that tuning call and freed before it
+ * returns; see proj_run), proj_run only enqueues work and returns: it never
  * synchronises, allocates or reads device memory on the host, so it may be
  * recorded into a HIP graph (stream capture) -- see "Capture" below.
  *
  * Memory the library owns: per context, the split-K workspace (exactly the
  * caller's bound, given to proj_create) and 1.25 KiB of zero page and sink;
- * per tuning call, the flush buffer above; per GPU, the 2 MiB static array
+ * per tuning call, the flush buffer and operand copies above; per GPU, the 2 MiB static array
  * of split-K partials that proj_run_noalloc uses (part of the library's code
  * object, held until the process ends).  Nothing else.
  *
